@@ -1,0 +1,111 @@
+"""O2 — per-iteration bookkeeping of the reducer (TEST INFRASTRUCTURE ONLY).
+
+What the pages fix:
+  * each bucket counts the gradients it still waits for; every gradient-ready
+    hook decrements its bucket's count, and a bucket whose count reaches zero
+    is ready [DDP-ch17 §17.2, §17.12; L15 §2.3; PTD-notes §3.2];
+  * ready buckets are launched strictly by bucket index: bucket i+1 waits for
+    bucket i even when it filled first, because every process must issue the
+    collectives in the same order [DDP-ch17 §17.12; L15 §2.3, §8 exercise 6];
+  * the counts are reset before each backward (prepare_for_backward, run at
+    the end of forward) together with the per-iteration ready set
+    [DDP-ch17 §17.12, §17.16];
+  * marking one parameter ready twice in one backward is an error
+    [DDP-ch17 §17.16];
+  * starting a new iteration while the previous one still has buckets that
+    never launched is an error that names the parameters which got no
+    gradient [DDP-ch17 §17.6; L15 §4.2];
+  * the end of backward waits for every bucket's collective
+    [DDP-ch17 §17.41; MegatronDDP §2, §5].
+
+Reading: finishing an iteration whose buckets have not all launched is an
+error that lists, in ascending order, the parameters not marked ready.
+
+``comm_timeline`` is the lecture's alpha-beta overlap model: one compute
+stream yields gradients, one communication stream reduces buckets one at a
+time in bucket order, each costing alpha + beta * bytes [L15 §3.1, §8
+exercises 4-5].
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Tuple
+
+OK = 0
+ERR_INVALID = -1
+ERR_ALREADY_READY = -2
+ERR_UNFINISHED = -3
+ERR_NOT_READY = -4
+
+
+class ModelError(Exception):
+    def __init__(self, code: int, params: Sequence[int] = ()):
+        super().__init__(code, list(params))
+        self.code = code
+        self.params = list(params)
+
+
+class ReducerModel:
+    def __init__(self, buckets: Sequence[Sequence[int]], n_params: int):
+        self.buckets = [list(b) for b in buckets]
+        self.P = n_params
+        self.bucket_of = [-1] * n_params
+        for b, members in enumerate(self.buckets):
+            for p in members:
+                self.bucket_of[p] = b
+        if any(b < 0 for b in self.bucket_of):
+            raise ModelError(ERR_INVALID)
+        self.launched: List[int] = []      # every launch since construction
+        self._reset()
+
+    def _reset(self) -> None:
+        self.pending = [len(m) for m in self.buckets]
+        self.ready = [False] * self.P
+        self.next_bucket = 0
+        self.marks = 0
+        self.finished = False
+        self.ready_order: List[int] = []
+
+    def _unready(self) -> List[int]:
+        return [p for p in range(self.P) if not self.ready[p]]
+
+    def prepare_for_backward(self) -> None:
+        if self.marks > 0 and not self.finished:
+            raise ModelError(ERR_UNFINISHED, self._unready())
+        self._reset()
+
+    def mark_ready(self, p: int) -> List[int]:
+        """Returns the buckets this call launches, in launch order."""
+        if not 0 <= p < self.P:
+            raise ModelError(ERR_INVALID)
+        if self.ready[p]:
+            raise ModelError(ERR_ALREADY_READY, [p])
+        self.ready[p] = True
+        self.marks += 1
+        self.ready_order.append(p)
+        self.pending[self.bucket_of[p]] -= 1
+        out = []
+        while self.next_bucket < len(self.buckets) and self.pending[self.next_bucket] == 0:
+            out.append(self.next_bucket)
+            self.next_bucket += 1
+        self.launched += out
+        return out
+
+    def finish(self) -> None:
+        if self.next_bucket < len(self.buckets):
+            raise ModelError(ERR_NOT_READY, self._unready())
+        self.finished = True
+
+
+def comm_timeline(bucket_bytes: Sequence[float], bucket_ready: Sequence[float], alpha: float,
+                  beta: float) -> List[Tuple[float, float]]:
+    """(start, end) of each bucket's reduction on one serial communication
+    stream: bucket b starts when it is ready and bucket b-1 has ended, and
+    lasts alpha + beta * bytes."""
+    spans: List[Tuple[float, float]] = []
+    prev_end = float("-inf")
+    for nbytes, ready in zip(bucket_bytes, bucket_ready):
+        start = max(ready, prev_end)
+        end = start + alpha + beta * nbytes
+        spans.append((start, end))
+        prev_end = end
+    return spans

@@ -1,0 +1,69 @@
+"""O4 — literal ring all-reduce simulation (TEST INFRASTRUCTURE ONLY).
+
+Simulates W ranks on a ring, step by step, as [DDP-ch17 §17.4] describes:
+the buffer is cut into W chunks; in each of W-1 reduce-scatter steps every
+rank passes one chunk to its successor, which adds it to its own copy; after
+them each rank owns one fully reduced chunk, and W-1 all-gather steps pass the
+reduced chunks around the ring until every rank holds all of them. Each rank
+first scales its gradient by 1/W while copying it into the bucket
+[DDP-ch17 §17.9].
+
+Readings (where the pages are silent): chunk size ceil(n/W); at step s of
+either phase, rank r sends chunk (r - s) mod W (reduce-scatter) or
+(r + 1 - s) mod W (all-gather) to rank (r + 1) mod W, using the values it
+held before the step. All arithmetic is numpy float32 (IEEE, round to
+nearest even).
+
+Meant for tiny inputs only; used to check the fold in fold.c, not as a
+reference for large buckets.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+
+def _chunks(n: int, W: int):
+    q = -(-n // W) if n else 0
+    return [(min(c * q, n), min((c + 1) * q, n)) for c in range(W)]
+
+
+def ring_allreduce(grads: Sequence[np.ndarray], wgrad_bf16: Optional[Sequence[np.ndarray]] = None) -> List[np.ndarray]:
+    """Returns every rank's buffer after the all-gather.
+
+    grads: W float32 arrays (the fp32 gradients, or the main_grad values when
+    wgrad_bf16 is given). wgrad_bf16: W uint16 arrays of bf16 bit patterns,
+    added in fp32 to grads before scaling."""
+    W = len(grads)
+    n = grads[0].size
+    s = np.float32(1.0) / np.float32(W)
+    bufs = []
+    for r in range(W):
+        g = np.array(grads[r], dtype=np.float32, copy=True)
+        if wgrad_bf16 is not None:
+            wide = (np.asarray(wgrad_bf16[r], dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+            g = (g + wide).astype(np.float32)
+        bufs.append((g * s).astype(np.float32))
+    ch = _chunks(n, W)
+
+    # reduce-scatter
+    for step in range(W - 1):
+        sends = []
+        for r in range(W):
+            c = (r - step) % W
+            lo, hi = ch[c]
+            sends.append(((r + 1) % W, lo, hi, bufs[r][lo:hi].copy()))
+        for dst, lo, hi, data in sends:
+            bufs[dst][lo:hi] = (bufs[dst][lo:hi] + data).astype(np.float32)
+
+    # all-gather
+    for step in range(W - 1):
+        sends = []
+        for r in range(W):
+            c = (r + 1 - step) % W
+            lo, hi = ch[c]
+            sends.append(((r + 1) % W, lo, hi, bufs[r][lo:hi].copy()))
+        for dst, lo, hi, data in sends:
+            bufs[dst][lo:hi] = data
+    return bufs
