@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Throughput of bucketed gradient reduction on one MI355X.
+
+One step is one backward's worth of the data-parallel hot path through the C
+ABI: ddp_prepare_for_backward, ddp_mark_ready for every gradient in reverse
+registration order (each bucket launches on the side stream, after a wait on
+the compute stream, as soon as it and every earlier bucket are complete),
+and ddp_finish. Gradients are resident in HBM before the timed region; the
+bucket plan is made once, before it, as a reducer is built once per rebuild.
+
+Printed: one JSON line (stdout) with the effective HBM bandwidth of the step
+(algorithmic bytes: 8 per element and replica for fp32, 10 for bf16 wgrads
+into fp32 main_grad), the roofline of the bucket-reduce kernel from HIP
+events around every launch in the timed region, and the CPU oracle timed on
+a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "bucket all-reduce effective GB/s and % of MI355X HBM peak, 1 GPU"
+MODE_NAMES = {0: "f32_copy", 1: "f32_view", 2: "bf16_accum_f32"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("bucket_reduce.hip", "internal.h"):
+        with open(os.path.join(ROOT, "bucketed_gradient_all_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Per-launch HBM bytes from rocprofv3 counters committed under
+    profiles/, only if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"bucket_reduce_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Session:
+    def __init__(self, wl):
+        import numpy as np
+        import torch
+
+        import bucketed_gradient_all_amd as ddp
+        from synth.device import DeviceInputs
+
+        self.torch, self.ddp, self.wl = torch, ddp, wl
+        self.plan = ddp.ddp_plan_buckets(wl.param_bytes, wl.order_mode, wl.cap_bytes, wl.first_cap_bytes)
+        bb = [int(x) for x in self.plan.bucket_bytes]
+        starts = np.concatenate([[0], np.cumsum(bb)])[:-1]
+        flat_off = [int(starts[self.plan.bucket_of[p]] + self.plan.offset_in_bucket[p]) // 4
+                    for p in range(len(wl.numel))]
+        self.total = sum(bb) // 4
+        self.bucket_bytes = bb
+        t0 = time.perf_counter()
+        self.inputs = DeviceInputs(wl, flat_off, self.total)
+        log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
+        self.compute = torch.cuda.Stream()
+        self.comm = torch.cuda.Stream()
+        self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
+                                  self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream)
+        self.order = list(range(len(wl.numel) - 1, -1, -1))
+        self.members = self.plan.buckets()
+
+    def step(self, backward_us: float = 0.0, serial: bool = False):
+        ddp = self.ddp
+        ddp.ddp_prepare_for_backward(self.r)
+        if backward_us <= 0:
+            for p in self.order:
+                ddp.ddp_mark_ready(self.r, p)
+        else:
+            import synth
+            tot = float(sum(self.bucket_bytes)) or 1.0
+            cs = self.compute.cuda_stream
+            if serial:
+                synth.spin_dev(backward_us, cs)
+            for b, members in enumerate(self.members):
+                if not serial:
+                    synth.spin_dev(backward_us * self.bucket_bytes[b] / tot, cs)
+                for p in members:
+                    ddp.ddp_mark_ready(self.r, p)
+        ddp.ddp_finish(self.r, host_blocking=False)
+
+    def timed(self, steps: int, **kw):
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(**kw)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, session, target_s: float):
+    """The oracle (threaded fold, as written) on the first buckets of the
+    same workload, inputs regenerated on the host; only the fold is timed."""
+    import numpy as np
+
+    import synth
+    from oracle import fold
+    from oracle.plan import plan_buckets
+    from synth.workloads import IN_BF16_ACCUM_F32, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD
+
+    oplan = plan_buckets(wl.param_bytes, wl.order_mode, cap=wl.cap_bytes, first_cap=wl.first_cap_bytes)
+    per_elem = 10 if wl.input_mode == IN_BF16_ACCUM_F32 else 8
+    budget_bytes = 2.0e9          # algorithmic bytes of the sample (bounded host memory)
+    chosen, acc = [], 0
+    for b in range(oplan.n_buckets):
+        nb = per_elem * wl.world * oplan.bucket_bytes[b] // 4
+        if chosen and acc + nb > budget_bytes:
+            break
+        chosen.append(b)
+        acc += nb
+    sc = synth.scale_for(wl.dist, wl.sigma)
+    threads = max(1, min(host_cores(), 64))
+
+    def gen_bucket(b):
+        n = oplan.bucket_bytes[b] // 4
+        xs, gs = [], []
+        for w in range(wl.world):
+            x = np.empty(n, np.float32)
+            g = np.empty(n, np.uint16) if wl.input_mode == IN_BF16_ACCUM_F32 else None
+            for p in oplan.buckets[b]:
+                o, m = oplan.offset_in_bucket[p] // 4, wl.numel[p]
+                if wl.input_mode == IN_BF16_ACCUM_F32:
+                    x[o:o + m] = synth.host_f32(synth.key(wl.seed, STREAM_MAIN, w, p), wl.dist, sc, m)
+                    g[o:o + m] = synth.host_bf16(synth.key(wl.seed, STREAM_WGRAD, w, p), wl.dist, sc, m)
+                else:
+                    x[o:o + m] = synth.host_f32(synth.key(wl.seed, STREAM_GRAD, w, p), wl.dist, sc, m)
+            xs.append(x)
+            gs.append(g)
+        return xs, gs
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        data = list(ex.map(gen_bucket, chosen))
+    log(f"[bench] cpu baseline: generated {len(chosen)} buckets in {time.perf_counter() - t0:.1f} s")
+
+    def run(nthreads):
+        outs = []
+        t = time.perf_counter()
+        for xs, gs in data:
+            if wl.input_mode == IN_BF16_ACCUM_F32:
+                outs.append(fold.reduce_bf16acc(xs, gs, nthreads=nthreads))
+            else:
+                outs.append(fold.reduce_f32(xs, nthreads=nthreads))
+        return time.perf_counter() - t, outs
+
+    t1, outs = run(0)
+    reps_mt, tmt = 0, 0.0
+    while tmt < max(1.0, target_s - t1) and reps_mt < 2000:
+        dt, outs_mt = run(threads)
+        tmt += dt
+        reps_mt += 1
+    gbps_1 = acc / t1 / 1e9
+    gbps_mt = acc * reps_mt / tmt / 1e9
+    match = None
+    if session is not None:
+        match = True
+        for b, out in zip(chosen, outs):
+            lo = sum(oplan.bucket_bytes[:b]) // 4
+            got = session.inputs.flat[0][lo:lo + out.size].cpu().numpy()
+            match &= bool(np.array_equal(got.view(np.uint32), out.view(np.uint32)))
+    n_elems = sum(oplan.bucket_bytes[b] for b in chosen) // 4
+    return {
+        "value": round(gbps_mt, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"buckets 0..{chosen[-1]} of {oplan.n_buckets} ({n_elems} elements x W={wl.world}, "
+                  f"{acc / 1e9:.2f} GB algorithmic), threaded fold x{reps_mt}; inputs regenerated on the host, "
+                  f"generation untimed",
+        "single_thread_value": round(gbps_1, 3),
+        "cpu_seconds": round(t1 + tmt, 2),
+        "gpu_matches_oracle_on_sample": match,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="resnet50",
+                    help="tiny | resnet50 | bert_large | megatron_llama1b | sweep_w{W}_cap{MiB}")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-ms", type=float, default=20.0,
+                    help="synthetic backward for the overlap measurement (0 disables it)")
+    ap.add_argument("--overlap-steps", type=int, default=5)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain copy of this size (for HBM counter calibration) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the W data-parallel replicas are buffers in that GPU's HBM, "
+              "so runs on more than one GPU are not part of this benchmark (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from synth import workloads as wls
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            synth.copy_dev(dst.data_ptr(), src.data_ptr(), nbytes, 0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            synth.copy_dev(dst.data_ptr(), src.data_ptr(), nbytes, 0)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        print(json.dumps({"copy_bytes": nbytes, "read_plus_write_GBps": round(2 * nbytes / dt / 1e9, 1)}))
+        return
+
+    wl = wls.by_name(args.workload)
+    log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
+        f"mode={MODE_NAMES[wl.input_mode]}")
+    s = Session(wl)
+    import bucketed_gradient_all_amd as ddp
+    bytes_per_step = wl.algorithmic_bytes()
+
+    for _ in range(args.warmup):
+        s.step()
+    torch.cuda.synchronize()
+    ddp.ddp_set_timing(s.r, True)
+    log(f"[bench] timing {args.steps} steps")
+    elapsed = s.timed(args.steps)
+    buckets, ms = ddp.ddp_get_timings(s.r)
+    ddp.ddp_set_timing(s.r, False)
+    step_s = elapsed / args.steps
+    value = bytes_per_step / step_s / 1e9
+    kernel_s = float(ms.sum()) / 1e3
+    launches = len(ms)
+    per_launch_bytes = bytes_per_step * args.steps / max(launches, 1)
+    achieved = bytes_per_step * args.steps / kernel_s / 1e9 if kernel_s > 0 else 0.0
+    W = wl.world
+    bus = sum(2 * (W - 1) / W * b for b in s.bucket_bytes) / step_s / 1e9
+
+    # per-bucket kernel rates (median over steps)
+    import numpy as np
+    per_bucket = {}
+    for b in range(s.plan.n_buckets):
+        sel = ms[buckets == b]
+        if sel.size:
+            per_elem = 10 if wl.input_mode == 2 else 8
+            nb = per_elem * W * s.bucket_bytes[b] // 4
+            per_bucket[b] = round(nb / (float(np.median(sel)) / 1e3) / 1e9, 1)
+
+    overlap = None
+    if args.backward_ms > 0:
+        us = args.backward_ms * 1e3
+        s.step(backward_us=us)
+        t_ov = s.timed(args.overlap_steps, backward_us=us) / args.overlap_steps
+        t_se = s.timed(args.overlap_steps, backward_us=us, serial=True) / args.overlap_steps
+        overlap = {"backward_ms": args.backward_ms, "step_ms_overlapped": round(t_ov * 1e3, 3),
+                   "step_ms_serial": round(t_se * 1e3, 3),
+                   "exposed_ms": round(t_ov * 1e3 - args.backward_ms, 3),
+                   "reduce_ms_alone": round(step_s * 1e3, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        s.inputs.refill()
+        s.step()
+        torch.cuda.synchronize()
+        cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds)
+
+    traffic = measured_traffic(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.input_mode != 2 else "bf16+f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "world": W, "tensors": len(wl.numel), "elements": wl.total_numel,
+                   "buckets": s.plan.n_buckets, "cap_bytes": wl.cap_bytes, "first_cap_bytes": wl.first_cap_bytes,
+                   "input_mode": MODE_NAMES[wl.input_mode], "bytes_per_step": bytes_per_step,
+                   "parallelism": "1 GPU, W replicas in HBM"},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "bus_bw_GBps": round(bus, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "bucket_reduce (reduce_fixed)", "launches": launches,
+                     "algorithmic_bytes_per_launch": int(per_launch_bytes),
+                     "avg_launch_us": round(kernel_s / max(launches, 1) * 1e6, 2),
+                     "per_bucket_GBps": per_bucket},
+        "overlap": overlap,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    ddp.ddp_reducer_destroy(s.r)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,312 @@
+"""Python binding of libddp.so (include/ddp.h): bucketed gradient reduction
+for data-parallel training on MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the C++ host
+library and its HIP kernels. The functions keep the C names; a negative
+status raises DDPError carrying the code and the library's message. There is
+no fallback: if libddp.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Callable, List, NamedTuple, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libddp.so")
+CSRC = os.path.join(HERE, "csrc")
+
+DDP_OK = 0
+DDP_ERR_INVALID = -1
+DDP_ERR_ALREADY_READY = -2
+DDP_ERR_UNFINISHED = -3
+DDP_ERR_NOT_READY = -4
+DDP_ERR_ORDER = -5
+DDP_ERR_HIP = -6
+DDP_ERR_HOOK = -7
+
+DDP_ORDER_REVERSE = 0
+DDP_ORDER_GIVEN = 1
+DDP_ORDER_FWD_THEN_REVERSE = 2
+
+DDP_IN_F32_COPY = 0
+DDP_IN_F32_VIEW = 1
+DDP_IN_BF16_ACCUM_F32 = 2
+
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
+               "-ffp-contract=off", "-fno-fast-math",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> None:
+    """Compile libddp.so in place with hipcc for gfx950."""
+    srcs = [os.path.join(CSRC, "reducer.cpp"), os.path.join(CSRC, "bucket_reduce.hip")]
+    cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-o", LIB_PATH + ".tmp", *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=HERE)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+
+
+class DDPError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+        self.msg = msg
+
+
+HOOK_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32)
+
+
+class ddp_reducer_desc(ctypes.Structure):
+    _fields_ = [
+        ("world", ctypes.c_int32),
+        ("n_params", ctypes.c_int32),
+        ("param_numel", ctypes.c_void_p),
+        ("bucket_of", ctypes.c_void_p),
+        ("offset_in_bucket", ctypes.c_void_p),
+        ("n_buckets", ctypes.c_int32),
+        ("input_mode", ctypes.c_int32),
+        ("grads", ctypes.c_void_p),
+        ("flat", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("compute_stream", ctypes.c_void_p),
+        ("comm_stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        sig = {
+            "ddp_plan_buckets": [I32, P, P, I32, I64, I64, P, P, P, P, P, P],
+            "ddp_reducer_create": [ctypes.POINTER(ddp_reducer_desc), ctypes.POINTER(ctypes.c_void_p)],
+            "ddp_reducer_destroy": [P],
+            "ddp_prepare_for_backward": [P],
+            "ddp_mark_ready": [P, I32],
+            "ddp_bucket_reduce": [P, I32, P],
+            "ddp_finish": [P, I32],
+            "ddp_register_comm_hook": [P, HOOK_FN, P],
+            "ddp_get_bucket": [P, I32, P, P, P],
+            "ddp_get_bucket_params": [P, I32, P],
+            "ddp_get_ready_order": [P, P, P],
+            "ddp_get_launched": [P, P],
+            "ddp_set_timing": [P, I32],
+            "ddp_get_timings": [P, P, P, I32, P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.ddp_workspace_bytes.argtypes = [ctypes.POINTER(ddp_reducer_desc)]
+        L.ddp_workspace_bytes.restype = ctypes.c_size_t
+        L.ddp_last_error.argtypes = []
+        L.ddp_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def ddp_last_error() -> str:
+    return lib().ddp_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise DDPError(rc, ddp_last_error())
+    return rc
+
+
+class BucketPlan(NamedTuple):
+    bucket_of: np.ndarray        # [P] int32
+    offset_in_bucket: np.ndarray  # [P] int64 bytes
+    bucket_params: np.ndarray    # [P] int32, bucket by bucket
+    bucket_nparams: np.ndarray   # [B] int32
+    bucket_bytes: np.ndarray     # [B] int64
+    n_buckets: int
+
+    def buckets(self) -> List[List[int]]:
+        out, k = [], 0
+        for c in self.bucket_nparams:
+            out.append([int(p) for p in self.bucket_params[k:k + c]])
+            k += c
+        return out
+
+
+def ddp_plan_buckets(param_bytes: Sequence[int], order_mode: int = DDP_ORDER_REVERSE,
+                     cap_bytes: int = 25 << 20, first_cap_bytes: int = 1 << 20,
+                     order: Optional[Sequence[int]] = None) -> BucketPlan:
+    pb = np.ascontiguousarray(param_bytes, dtype=np.int64)
+    P = pb.size
+    od = np.ascontiguousarray(order if order is not None else [], dtype=np.int32)
+    bucket_of = np.empty(P, np.int32)
+    offset = np.empty(P, np.int64)
+    bparams = np.empty(P, np.int32)
+    bn = np.empty(max(P, 1), np.int32)
+    bb = np.empty(max(P, 1), np.int64)
+    nb = ctypes.c_int32(0)
+    _check(lib().ddp_plan_buckets(P, pb.ctypes.data, od.ctypes.data if order is not None else None, order_mode,
+                                  cap_bytes, first_cap_bytes, bucket_of.ctypes.data, offset.ctypes.data,
+                                  bparams.ctypes.data, bn.ctypes.data, bb.ctypes.data, ctypes.byref(nb)))
+    B = nb.value
+    return BucketPlan(bucket_of, offset, bparams, bn[:B].copy(), bb[:B].copy(), B)
+
+
+class Desc:
+    """Owns the host arrays a ddp_reducer_desc points to."""
+
+    def __init__(self, world: int, param_numel: Sequence[int], bucket_of: Sequence[int],
+                 offset_in_bucket: Sequence[int], n_buckets: int, input_mode: int = DDP_IN_F32_COPY,
+                 grads: Optional[Sequence[Sequence[int]]] = None, flat: Optional[Sequence[int]] = None,
+                 workspace: int = 0, workspace_bytes: int = 0, compute_stream: int = 0, comm_stream: int = 0):
+        self.numel = np.ascontiguousarray(param_numel, dtype=np.int64)
+        self.bucket_of = np.ascontiguousarray(bucket_of, dtype=np.int32)
+        self.offset = np.ascontiguousarray(offset_in_bucket, dtype=np.int64)
+        P = self.numel.size
+        self.grads = None
+        if grads is not None:
+            self.grads = np.ascontiguousarray(np.asarray(grads, dtype=np.uint64).reshape(world * P)
+                                              if P else np.zeros(1, np.uint64))
+        self.flat = np.ascontiguousarray(flat, dtype=np.uint64) if flat is not None else None
+        d = ddp_reducer_desc()
+        d.world = world
+        d.n_params = P
+        d.param_numel = self.numel.ctypes.data
+        d.bucket_of = self.bucket_of.ctypes.data
+        d.offset_in_bucket = self.offset.ctypes.data
+        d.n_buckets = n_buckets
+        d.input_mode = input_mode
+        d.grads = self.grads.ctypes.data if self.grads is not None else None
+        d.flat = self.flat.ctypes.data if self.flat is not None else None
+        d.workspace = workspace or None
+        d.workspace_bytes = workspace_bytes
+        d.compute_stream = compute_stream or None
+        d.comm_stream = comm_stream or None
+        self.c = d
+
+    def set_workspace(self, ptr: int, nbytes: int) -> None:
+        self.c.workspace = ptr or None
+        self.c.workspace_bytes = nbytes
+
+
+def ddp_workspace_bytes(desc: Desc) -> int:
+    n = lib().ddp_workspace_bytes(ctypes.byref(desc.c))
+    if n == 0:
+        raise DDPError(DDP_ERR_INVALID, ddp_last_error())
+    return int(n)
+
+
+class Reducer:
+    """Handle of a ddp_reducer plus the objects it must keep alive."""
+
+    def __init__(self, handle: int, desc: Desc):
+        self.handle = handle
+        self.desc = desc
+        self._hook = None
+
+
+def ddp_reducer_create(desc: Desc) -> Reducer:
+    h = ctypes.c_void_p()
+    _check(lib().ddp_reducer_create(ctypes.byref(desc.c), ctypes.byref(h)))
+    return Reducer(h.value, desc)
+
+
+def ddp_reducer_destroy(r: Reducer) -> None:
+    if r.handle:
+        _check(lib().ddp_reducer_destroy(r.handle))
+        r.handle = None
+
+
+def ddp_prepare_for_backward(r: Reducer) -> None:
+    _check(lib().ddp_prepare_for_backward(r.handle))
+
+
+def ddp_mark_ready(r: Reducer, param: int) -> None:
+    _check(lib().ddp_mark_ready(r.handle, param))
+
+
+def ddp_bucket_reduce(r: Reducer, bucket: int, stream: int) -> None:
+    _check(lib().ddp_bucket_reduce(r.handle, bucket, stream or None))
+
+
+def ddp_finish(r: Reducer, host_blocking: bool = False) -> None:
+    _check(lib().ddp_finish(r.handle, 1 if host_blocking else 0))
+
+
+def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> None:
+    """fn(bucket) -> int; None restores the default reduction."""
+    if fn is None:
+        r._hook = None
+        _check(lib().ddp_register_comm_hook(r.handle, HOOK_FN(), None))
+        return
+    r._hook = HOOK_FN(lambda ctx, b: int(fn(b)))
+    _check(lib().ddp_register_comm_hook(r.handle, r._hook, None))
+
+
+def ddp_get_bucket(r: Reducer, bucket: int):
+    nbytes, off, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(lib().ddp_get_bucket(r.handle, bucket, ctypes.byref(nbytes), ctypes.byref(off), ctypes.byref(n)))
+    return nbytes.value, off.value, n.value
+
+
+def ddp_get_bucket_params(r: Reducer, bucket: int) -> List[int]:
+    n = ddp_get_bucket(r, bucket)[2]
+    out = np.empty(max(n, 1), np.int32)
+    _check(lib().ddp_get_bucket_params(r.handle, bucket, out.ctypes.data))
+    return [int(x) for x in out[:n]]
+
+
+def ddp_get_ready_order(r: Reducer) -> List[int]:
+    out = np.empty(max(r.desc.numel.size, 1), np.int32)
+    n = ctypes.c_int32()
+    _check(lib().ddp_get_ready_order(r.handle, out.ctypes.data, ctypes.byref(n)))
+    return [int(x) for x in out[:n.value]]
+
+
+def ddp_get_launched(r: Reducer) -> int:
+    n = ctypes.c_int32()
+    _check(lib().ddp_get_launched(r.handle, ctypes.byref(n)))
+    return n.value
+
+
+def ddp_set_timing(r: Reducer, enable: bool) -> None:
+    _check(lib().ddp_set_timing(r.handle, 1 if enable else 0))
+
+
+def ddp_get_timings(r: Reducer):
+    """(bucket indices, kernel ms) of every launch since timing was enabled."""
+    n = ctypes.c_int32()
+    _check(lib().ddp_get_timings(r.handle, None, None, 0, ctypes.byref(n)))
+    b = np.empty(max(n.value, 1), np.int32)
+    ms = np.empty(max(n.value, 1), np.float32)
+    _check(lib().ddp_get_timings(r.handle, b.ctypes.data, ms.ctypes.data, n.value, ctypes.byref(n)))
+    return b[:n.value].copy(), ms[:n.value].copy()
+
+
+def make_reducer(world: int, param_numel: Sequence[int], plan: BucketPlan, input_mode: int,
+                 grad_ptrs: Optional[Sequence[Sequence[int]]], flat_ptrs: Sequence[int],
+                 compute_stream: int, comm_stream: int) -> Reducer:
+    """Creates a device reducer; the workspace is a torch allocation kept
+    alive by the returned handle."""
+    import torch
+
+    desc = Desc(world, param_numel, plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, input_mode,
+                grads=grad_ptrs, flat=flat_ptrs, compute_stream=compute_stream, comm_stream=comm_stream)
+    nbytes = ddp_workspace_bytes(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    desc.set_workspace(ws.data_ptr(), nbytes)
+    r = ddp_reducer_create(desc)
+    r.workspace = ws
+    return r

@@ -1,0 +1,54 @@
+// Internal types shared by the host reducer (reducer.cpp) and the bucket
+// reduction kernels (bucket_reduce.hip). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace ddp {
+
+constexpr int kThreads = 256;   // one workgroup = four wave64s
+
+// Vector groups (of 4 elements) each thread carries per replica. More groups
+// give more loads in flight per wave; W groups' worth of registers are held
+// per unit, so the count shrinks as W grows.
+constexpr int unroll_for(int W)
+{
+    return W <= 4 ? 4 : (W <= 8 ? 2 : 1);
+}
+
+// Elements one workgroup covers (one tile).
+constexpr int64_t tile_elems(int W)
+{
+    return int64_t(kThreads) * 4 * unroll_for(W);
+}
+
+// A run of bucket elements that lies inside one gradient tensor and one ring
+// chunk, so every element in it has the same source tensor and the same fold
+// order.
+struct DeviceSeg {
+    int64_t flat;    // first element in the flat buffers
+    int64_t src;     // first element inside the source gradient (COPY, BF16_ACCUM)
+    int64_t len;     // elements
+    int32_t param;   // source gradient (COPY, BF16_ACCUM); -1 for VIEW
+    int32_t chunk;   // ring chunk c: the fold starts at replica c
+    int32_t tile0;   // first tile of this segment
+    int32_t head;    // scalar elements before the 16-byte aligned body, or -1:
+                     // the segment is processed one element per lane
+};
+
+struct KernelTables {
+    const DeviceSeg *segs;
+    const int32_t *tile_seg;       // tile -> segment
+    const void *const *grads;      // [W*P] replica-major source pointers (COPY, BF16_ACCUM)
+    float *const *flat;            // [W] flat buffers
+    int32_t n_params;
+};
+
+// Enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on stream s.
+// Returns hipSuccess or the launch error.
+hipError_t launch_bucket_reduce(int mode, int W, float scale, const KernelTables &t, int32_t tile_begin,
+                                int32_t n_tiles, hipStream_t s);
+
+}  // namespace ddp

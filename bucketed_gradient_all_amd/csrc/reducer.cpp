@@ -1,0 +1,608 @@
+// Host half of libddp: bucket planning, the per-iteration reducer state
+// machine and the launcher that feeds the bucket reduction kernels.
+//
+// Sources are cited by tag and section; the tags are defined in include/ddp.h.
+#include "../../include/ddp.h"
+#include "internal.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+#include <vector>
+
+using ddp::DeviceSeg;
+using ddp::KernelTables;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg)
+{
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(const char *what, hipError_t e)
+{
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return DDP_ERR_HIP;
+}
+
+std::string list_params(const std::vector<int32_t> &ps)
+{
+    std::string s;
+    size_t shown = 0;
+    for (int32_t p : ps) {
+        if (shown == 64) {
+            s += " ... (" + std::to_string(ps.size()) + " in all)";
+            break;
+        }
+        s += (shown ? " " : "") + std::to_string(p);
+        ++shown;
+    }
+    return s;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x)
+{
+    return (x + kAlign - 1) / kAlign * kAlign;
+}
+
+// Plan data validated and normalised from a desc.
+struct PlanView {
+    int32_t W = 0, P = 0, B = 0, mode = 0;
+    std::vector<int64_t> numel;
+    std::vector<int32_t> bucket_of;
+    std::vector<int64_t> offset;                 // bytes inside the bucket
+    std::vector<std::vector<int32_t>> members;   // flat-buffer order
+    std::vector<int64_t> bucket_bytes, bucket_flat;
+    // device tables (built only when buffers are given)
+    std::vector<DeviceSeg> segs;
+    std::vector<int32_t> tile_seg;
+    std::vector<int32_t> tile_begin, tile_count;
+};
+
+// Segments of every bucket: runs inside one gradient and one ring chunk. The
+// chunk of bucket element e is e / q with q = ceil(n / W) [DDP-ch17 §17.4].
+int build_segments(PlanView &pv, bool split_by_param)
+{
+    const int64_t TILE = ddp::tile_elems(pv.W);
+    pv.segs.clear();
+    pv.tile_seg.clear();
+    pv.tile_begin.assign(pv.B, 0);
+    pv.tile_count.assign(pv.B, 0);
+    int64_t tiles = 0;
+    auto add = [&](int b, int64_t flat, int64_t src, int64_t len, int32_t param, int32_t chunk) -> bool {
+        if (len <= 0) return true;
+        DeviceSeg s{};
+        s.flat = flat;
+        s.src = src;
+        s.len = len;
+        s.param = param;
+        s.chunk = chunk;
+        s.tile0 = int32_t(tiles);
+        s.head = -1;
+        int64_t nt = (len + TILE - 1) / TILE;
+        if (tiles + nt > std::numeric_limits<int32_t>::max()) return false;
+        int32_t id = int32_t(pv.segs.size());
+        pv.segs.push_back(s);
+        for (int64_t t = 0; t < nt; ++t) pv.tile_seg.push_back(id);
+        tiles += nt;
+        pv.tile_count[b] += int32_t(nt);
+        return true;
+    };
+    for (int b = 0; b < pv.B; ++b) {
+        pv.tile_begin[b] = int32_t(tiles);
+        const int64_t n = pv.bucket_bytes[b] / 4;
+        const int64_t base = pv.bucket_flat[b] / 4;
+        if (n == 0) continue;
+        const int64_t q = (n + pv.W - 1) / pv.W;
+        if (!split_by_param) {
+            for (int c = 0; c < pv.W; ++c) {
+                int64_t lo = std::min(n, int64_t(c) * q), hi = std::min(n, int64_t(c + 1) * q);
+                if (!add(b, base + lo, 0, hi - lo, -1, c)) return fail(DDP_ERR_INVALID, "too many tiles");
+            }
+            continue;
+        }
+        for (int32_t p : pv.members[b]) {
+            const int64_t a = pv.offset[p] / 4, len = pv.numel[p];
+            int64_t i = 0;
+            while (i < len) {
+                const int64_t e = a + i;
+                const int32_t c = int32_t(e / q);
+                const int64_t run = std::min(len - i, int64_t(c + 1) * q - e);
+                if (!add(b, base + e, i, run, p, c)) return fail(DDP_ERR_INVALID, "too many tiles");
+                i += run;
+            }
+        }
+    }
+    return DDP_OK;
+}
+
+int validate(const ddp_reducer_desc *d, PlanView &pv)
+{
+    if (!d) return fail(DDP_ERR_INVALID, "desc is NULL");
+    if (d->world < 1 || d->world > 1024) return fail(DDP_ERR_INVALID, "world must be in [1, 1024]");
+    if (d->n_params < 0 || d->n_buckets < 0) return fail(DDP_ERR_INVALID, "negative parameter or bucket count");
+    if (d->input_mode < DDP_IN_F32_COPY || d->input_mode > DDP_IN_BF16_ACCUM_F32)
+        return fail(DDP_ERR_INVALID, "unknown input mode");
+    if (d->n_params > 0 && (!d->param_numel || !d->bucket_of || !d->offset_in_bucket))
+        return fail(DDP_ERR_INVALID, "plan arrays are NULL");
+    pv.W = d->world;
+    pv.P = d->n_params;
+    pv.B = d->n_buckets;
+    pv.mode = d->input_mode;
+    pv.numel.assign(d->param_numel, d->param_numel + pv.P);
+    pv.bucket_of.assign(d->bucket_of, d->bucket_of + pv.P);
+    pv.offset.assign(d->offset_in_bucket, d->offset_in_bucket + pv.P);
+    pv.members.assign(pv.B, {});
+    for (int32_t p = 0; p < pv.P; ++p) {
+        if (pv.numel[p] < 0 || pv.numel[p] > (std::numeric_limits<int64_t>::max() >> 3))
+            return fail(DDP_ERR_INVALID, "gradient " + std::to_string(p) + " has a bad size");
+        if (pv.bucket_of[p] < 0 || pv.bucket_of[p] >= pv.B)
+            return fail(DDP_ERR_INVALID, "gradient " + std::to_string(p) + " has no valid bucket");
+        if (pv.offset[p] < 0 || pv.offset[p] % 4)
+            return fail(DDP_ERR_INVALID, "gradient " + std::to_string(p) + " has a bad offset");
+        pv.members[pv.bucket_of[p]].push_back(p);
+    }
+    pv.bucket_bytes.assign(pv.B, 0);
+    pv.bucket_flat.assign(pv.B, 0);
+    int64_t running = 0;
+    for (int b = 0; b < pv.B; ++b) {
+        auto &m = pv.members[b];
+        if (m.empty()) return fail(DDP_ERR_INVALID, "bucket " + std::to_string(b) + " holds no gradient");
+        std::stable_sort(m.begin(), m.end(), [&](int32_t x, int32_t y) {
+            return pv.offset[x] != pv.offset[y] ? pv.offset[x] < pv.offset[y] : pv.numel[x] < pv.numel[y];
+        });
+        int64_t off = 0;
+        for (int32_t p : m) {
+            if (pv.offset[p] != off)
+                return fail(DDP_ERR_INVALID, "bucket " + std::to_string(b) + ": gradients do not tile the bucket");
+            off += 4 * pv.numel[p];
+        }
+        pv.bucket_bytes[b] = off;
+        pv.bucket_flat[b] = running;
+        running += off;
+        if (running < 0) return fail(DDP_ERR_INVALID, "flat buffer too large");
+    }
+    return DDP_OK;
+}
+
+struct Layout {
+    size_t grads_off = 0, flat_off = 0, segs_off = 0, tiles_off = 0, total = 0;
+};
+
+Layout layout_of(const PlanView &pv)
+{
+    Layout l;
+    size_t cur = 0;
+    l.grads_off = cur;
+    if (pv.mode != DDP_IN_F32_VIEW) cur = align_up(cur + sizeof(void *) * size_t(pv.W) * size_t(pv.P));
+    l.flat_off = cur;
+    cur = align_up(cur + sizeof(float *) * size_t(pv.W));
+    l.segs_off = cur;
+    cur = align_up(cur + sizeof(DeviceSeg) * pv.segs.size());
+    l.tiles_off = cur;
+    cur = align_up(cur + sizeof(int32_t) * pv.tile_seg.size());
+    l.total = cur;
+    return l;
+}
+
+}  // namespace
+
+struct ddp_reducer {
+    PlanView pv;
+    bool device = false;
+    float scale = 1.0f;
+    KernelTables tables{};
+    hipStream_t compute = nullptr, comm = nullptr;
+    hipEvent_t ev_ready = nullptr, ev_done = nullptr;
+    bool timing = false;
+    std::vector<hipEvent_t> t0, t1;       // event pool, reused across record lists
+    std::vector<int32_t> timed_bucket;    // bucket of each recorded launch
+    ddp_comm_hook_fn hook = nullptr;
+    void *hook_ctx = nullptr;
+    // per-iteration state [DDP-ch17 §17.12, §17.16]
+    std::vector<int32_t> pending;
+    std::vector<uint8_t> ready;
+    std::vector<int32_t> ready_order;
+    int32_t next = 0;
+    int64_t marks = 0;
+    bool finished = false;
+
+    void reset()
+    {
+        pending.resize(pv.B);
+        for (int b = 0; b < pv.B; ++b) pending[b] = int32_t(pv.members[b].size());
+        ready.assign(pv.P, 0);
+        ready_order.clear();
+        next = 0;
+        marks = 0;
+        finished = false;
+    }
+    std::vector<int32_t> unready() const
+    {
+        std::vector<int32_t> out;
+        for (int32_t p = 0; p < pv.P; ++p)
+            if (!ready[p]) out.push_back(p);
+        return out;
+    }
+    bool in_iteration() const { return marks > 0 && !finished; }
+};
+
+namespace {
+
+int enqueue_reduce(ddp_reducer *r, int32_t b, hipStream_t s)
+{
+    if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device buffers");
+    hipError_t e;
+    size_t slot = r->timed_bucket.size();
+    if (r->timing) {
+        while (r->t0.size() <= slot) {
+            hipEvent_t a = nullptr, c = nullptr;
+            e = hipEventCreate(&a);
+            if (e == hipSuccess) e = hipEventCreate(&c);
+            if (e != hipSuccess) {
+                if (a) (void)hipEventDestroy(a);
+                return hip_fail("hipEventCreate", e);
+            }
+            r->t0.push_back(a);
+            r->t1.push_back(c);
+        }
+        if ((e = hipEventRecord(r->t0[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
+    }
+    e = ddp::launch_bucket_reduce(r->pv.mode, r->pv.W, r->scale, r->tables, r->pv.tile_begin[b],
+                                  r->pv.tile_count[b], s);
+    if (e != hipSuccess) return hip_fail("bucket reduce launch", e);
+    if (r->timing) {
+        if ((e = hipEventRecord(r->t1[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
+        r->timed_bucket.push_back(b);
+    }
+    return DDP_OK;
+}
+
+// All-reduce of one bucket as issued by the reducer: the comm stream first
+// waits for everything queued on the compute stream (the bucket's gradients
+// were produced there), then the hook or the default reduction runs on it
+// [PTD-notes §2.3; MegatronDDP §3].
+int launch_bucket(ddp_reducer *r, int32_t b)
+{
+    if (r->device && r->compute != r->comm) {
+        hipError_t e = hipEventRecord(r->ev_ready, r->compute);
+        if (e == hipSuccess) e = hipStreamWaitEvent(r->comm, r->ev_ready, 0);
+        if (e != hipSuccess) return hip_fail("stream wait", e);
+    }
+    if (r->hook) {
+        int rc = r->hook(r->hook_ctx, b);
+        if (rc != 0) return fail(DDP_ERR_HOOK, "communication hook returned " + std::to_string(rc) +
+                                                   " for bucket " + std::to_string(b));
+        return DDP_OK;
+    }
+    if (!r->device) return fail(DDP_ERR_INVALID, "no device buffers and no communication hook");
+    return enqueue_reduce(r, b, r->comm);
+}
+
+void destroy_events(ddp_reducer *r)
+{
+    if (r->ev_ready) (void)hipEventDestroy(r->ev_ready);
+    if (r->ev_done) (void)hipEventDestroy(r->ev_done);
+    for (auto e : r->t0)
+        if (e) (void)hipEventDestroy(e);
+    for (auto e : r->t1)
+        if (e) (void)hipEventDestroy(e);
+    r->ev_ready = r->ev_done = nullptr;
+    r->t0.clear();
+    r->t1.clear();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ddp_last_error(void) { return g_err.c_str(); }
+
+int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t *order, int32_t order_mode,
+                     int64_t cap_bytes, int64_t first_cap_bytes, int32_t *bucket_of, int64_t *offset_in_bucket,
+                     int32_t *bucket_params, int32_t *bucket_nparams, int64_t *bucket_bytes, int32_t *n_buckets)
+{
+    if (!n_buckets) return fail(DDP_ERR_INVALID, "n_buckets is NULL");
+    if (n_params < 0 || (n_params > 0 && !param_bytes)) return fail(DDP_ERR_INVALID, "bad gradient sizes");
+    if (cap_bytes < 0 || first_cap_bytes < 0) return fail(DDP_ERR_INVALID, "caps must be non-negative");
+    for (int32_t p = 0; p < n_params; ++p)
+        if (param_bytes[p] < 0) return fail(DDP_ERR_INVALID, "gradient sizes must be non-negative");
+
+    // the walk order [DDP-ch17 §17.3.1, §17.13; L15 §2.2]
+    std::vector<int32_t> walk(n_params);
+    if (order_mode == DDP_ORDER_REVERSE) {
+        for (int32_t i = 0; i < n_params; ++i) walk[i] = n_params - 1 - i;
+    } else if (order_mode == DDP_ORDER_FWD_THEN_REVERSE) {
+        for (int32_t i = 0; i < n_params; ++i) walk[i] = i;
+    } else if (order_mode == DDP_ORDER_GIVEN) {
+        if (n_params > 0 && !order) return fail(DDP_ERR_INVALID, "order is NULL");
+        std::vector<uint8_t> seen(n_params, 0);
+        for (int32_t i = 0; i < n_params; ++i) {
+            if (order[i] < 0 || order[i] >= n_params || seen[order[i]])
+                return fail(DDP_ERR_INVALID, "order is not a permutation of the gradient indices");
+            seen[order[i]] = 1;
+            walk[i] = order[i];
+        }
+    } else {
+        return fail(DDP_ERR_INVALID, "unknown order mode");
+    }
+
+    // seal a bucket once its bytes reach its cap [DDP-ch17 §17.2; L15 §8 exercise 3]
+    std::vector<std::vector<int32_t>> buckets;
+    std::vector<int32_t> open;
+    int64_t open_bytes = 0;
+    for (int32_t p : walk) {
+        open.push_back(p);
+        open_bytes += param_bytes[p];
+        if (open_bytes >= (buckets.empty() ? first_cap_bytes : cap_bytes)) {
+            buckets.push_back(std::move(open));
+            open.clear();
+            open_bytes = 0;
+        }
+    }
+    if (!open.empty()) buckets.push_back(std::move(open));
+    if (order_mode == DDP_ORDER_FWD_THEN_REVERSE) std::reverse(buckets.begin(), buckets.end());
+
+    int32_t k = 0;
+    for (size_t b = 0; b < buckets.size(); ++b) {
+        int64_t off = 0;
+        for (int32_t p : buckets[b]) {
+            if (bucket_of) bucket_of[p] = int32_t(b);
+            if (offset_in_bucket) offset_in_bucket[p] = off;
+            if (bucket_params) bucket_params[k] = p;
+            ++k;
+            off += param_bytes[p];
+        }
+        if (bucket_nparams) bucket_nparams[b] = int32_t(buckets[b].size());
+        if (bucket_bytes) bucket_bytes[b] = off;
+    }
+    *n_buckets = int32_t(buckets.size());
+    return DDP_OK;
+}
+
+size_t ddp_workspace_bytes(const ddp_reducer_desc *desc)
+{
+    PlanView pv;
+    if (validate(desc, pv) != DDP_OK) return 0;
+    if (build_segments(pv, pv.mode != DDP_IN_F32_VIEW) != DDP_OK) return 0;
+    return layout_of(pv).total;
+}
+
+int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
+{
+    if (!out) return fail(DDP_ERR_INVALID, "out is NULL");
+    ddp_reducer *r = new (std::nothrow) ddp_reducer();
+    if (!r) return fail(DDP_ERR_INVALID, "out of host memory");
+    int rc = validate(desc, r->pv);
+    if (rc != DDP_OK) {
+        delete r;
+        return rc;
+    }
+    PlanView &pv = r->pv;
+    r->scale = 1.0f / float(pv.W);
+    r->device = desc->flat != nullptr;
+    r->compute = static_cast<hipStream_t>(desc->compute_stream);
+    r->comm = static_cast<hipStream_t>(desc->comm_stream);
+    if (r->device) {
+        const bool copy_src = pv.mode != DDP_IN_F32_VIEW;
+        rc = build_segments(pv, copy_src);
+        if (rc != DDP_OK) {
+            delete r;
+            return rc;
+        }
+        for (int w = 0; w < pv.W; ++w)
+            if (!desc->flat[w]) {
+                delete r;
+                return fail(DDP_ERR_INVALID, "flat buffer of replica " + std::to_string(w) + " is NULL");
+            }
+        if (copy_src) {
+            if (pv.P > 0 && !desc->grads) {
+                delete r;
+                return fail(DDP_ERR_INVALID, "gradient pointer table is NULL");
+            }
+            for (int w = 0; w < pv.W; ++w)
+                for (int32_t p = 0; p < pv.P; ++p)
+                    if (pv.numel[p] > 0 && !desc->grads[size_t(w) * pv.P + p]) {
+                        delete r;
+                        return fail(DDP_ERR_INVALID, "gradient pointer is NULL");
+                    }
+        }
+        const Layout lay = layout_of(pv);
+        if (!desc->workspace || desc->workspace_bytes < lay.total ||
+            reinterpret_cast<uintptr_t>(desc->workspace) % 16) {
+            delete r;
+            return fail(DDP_ERR_INVALID, "workspace missing, misaligned or smaller than " +
+                                             std::to_string(lay.total) + " bytes");
+        }
+        // 16-byte vectors where every replica's source and destination allow
+        // them: a segment whose element `head` is 16-byte aligned on the
+        // destination side must be aligned on every source too
+        bool flat_aligned = true;
+        for (int w = 0; w < pv.W; ++w) flat_aligned &= reinterpret_cast<uintptr_t>(desc->flat[w]) % 16 == 0;
+        for (DeviceSeg &s : pv.segs) {
+            if (!flat_aligned) continue;
+            int64_t head = (4 - (s.flat % 4)) % 4;
+            head = std::min(head, s.len);
+            bool ok = true;
+            if (copy_src) {
+                const uintptr_t vec = pv.mode == DDP_IN_BF16_ACCUM_F32 ? 8 : 16;
+                const uintptr_t esz = pv.mode == DDP_IN_BF16_ACCUM_F32 ? 2 : 4;
+                for (int w = 0; w < pv.W && ok; ++w) {
+                    uintptr_t a = reinterpret_cast<uintptr_t>(desc->grads[size_t(w) * pv.P + s.param]);
+                    ok = (a + esz * uintptr_t(s.src + head)) % vec == 0;
+                }
+            }
+            if (ok) s.head = int32_t(head);
+        }
+        std::vector<uint8_t> host(lay.total, 0);
+        if (copy_src)
+            std::memcpy(host.data() + lay.grads_off, desc->grads, sizeof(void *) * size_t(pv.W) * pv.P);
+        std::memcpy(host.data() + lay.flat_off, desc->flat, sizeof(float *) * size_t(pv.W));
+        std::memcpy(host.data() + lay.segs_off, pv.segs.data(), sizeof(DeviceSeg) * pv.segs.size());
+        std::memcpy(host.data() + lay.tiles_off, pv.tile_seg.data(), sizeof(int32_t) * pv.tile_seg.size());
+        hipError_t e = hipMemcpy(desc->workspace, host.data(), lay.total, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            delete r;
+            return hip_fail("workspace upload", e);
+        }
+        uint8_t *ws = static_cast<uint8_t *>(desc->workspace);
+        r->tables.grads = copy_src ? reinterpret_cast<const void *const *>(ws + lay.grads_off) : nullptr;
+        r->tables.flat = reinterpret_cast<float *const *>(ws + lay.flat_off);
+        r->tables.segs = reinterpret_cast<const DeviceSeg *>(ws + lay.segs_off);
+        r->tables.tile_seg = reinterpret_cast<const int32_t *>(ws + lay.tiles_off);
+        r->tables.n_params = pv.P;
+        e = hipEventCreateWithFlags(&r->ev_ready, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            destroy_events(r);
+            delete r;
+            return hip_fail("hipEventCreate", e);
+        }
+    }
+    r->reset();
+    *out = r;
+    return DDP_OK;
+}
+
+int ddp_reducer_destroy(ddp_reducer *r)
+{
+    if (!r) return DDP_OK;
+    destroy_events(r);
+    delete r;
+    return DDP_OK;
+}
+
+int ddp_prepare_for_backward(ddp_reducer *r)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (r->in_iteration())
+        return fail(DDP_ERR_UNFINISHED,
+                    "the previous iteration's reduction never finished before a new one was prepared; "
+                    "gradients never marked ready: " + list_params(r->unready()));
+    r->reset();
+    return DDP_OK;
+}
+
+int ddp_mark_ready(ddp_reducer *r, int32_t param)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (param < 0 || param >= r->pv.P) return fail(DDP_ERR_INVALID, "gradient index out of range");
+    if (r->ready[param])
+        return fail(DDP_ERR_ALREADY_READY,
+                    "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
+    r->ready[param] = 1;
+    r->ready_order.push_back(param);
+    ++r->marks;
+    --r->pending[r->pv.bucket_of[param]];
+    // launch strictly by bucket index [DDP-ch17 §17.12; L15 §2.3]
+    while (r->next < r->pv.B && r->pending[r->next] == 0) {
+        const int32_t b = r->next++;
+        int rc = launch_bucket(r, b);
+        if (rc != DDP_OK) return rc;
+    }
+    return DDP_OK;
+}
+
+int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (bucket < 0 || bucket >= r->pv.B) return fail(DDP_ERR_INVALID, "bucket index out of range");
+    if (r->in_iteration() && bucket >= r->next)
+        return fail(DDP_ERR_ORDER, "bucket " + std::to_string(bucket) + " still waits for gradients");
+    return enqueue_reduce(r, bucket, static_cast<hipStream_t>(stream));
+}
+
+int ddp_finish(ddp_reducer *r, int32_t host_blocking)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (r->next < r->pv.B)
+        return fail(DDP_ERR_NOT_READY,
+                    "buckets still wait for gradients never marked ready: " + list_params(r->unready()));
+    if (r->device) {
+        hipError_t e = hipEventRecord(r->ev_done, r->comm);
+        if (e == hipSuccess && r->compute != r->comm) e = hipStreamWaitEvent(r->compute, r->ev_done, 0);
+        if (e == hipSuccess && host_blocking) e = hipEventSynchronize(r->ev_done);
+        if (e != hipSuccess) return hip_fail("finish", e);
+    }
+    r->finished = true;
+    return DDP_OK;
+}
+
+int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    r->hook = fn;
+    r->hook_ctx = ctx;
+    return DDP_OK;
+}
+
+int ddp_get_bucket(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t *flat_offset_bytes,
+                   int32_t *n_params)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (bucket < 0 || bucket >= r->pv.B) return fail(DDP_ERR_INVALID, "bucket index out of range");
+    if (bytes) *bytes = r->pv.bucket_bytes[bucket];
+    if (flat_offset_bytes) *flat_offset_bytes = r->pv.bucket_flat[bucket];
+    if (n_params) *n_params = int32_t(r->pv.members[bucket].size());
+    return DDP_OK;
+}
+
+int ddp_get_bucket_params(const ddp_reducer *r, int32_t bucket, int32_t *params)
+{
+    if (!r || !params) return fail(DDP_ERR_INVALID, "NULL argument");
+    if (bucket < 0 || bucket >= r->pv.B) return fail(DDP_ERR_INVALID, "bucket index out of range");
+    std::copy(r->pv.members[bucket].begin(), r->pv.members[bucket].end(), params);
+    return DDP_OK;
+}
+
+int ddp_get_ready_order(const ddp_reducer *r, int32_t *order, int32_t *n)
+{
+    if (!r || !n) return fail(DDP_ERR_INVALID, "NULL argument");
+    *n = int32_t(r->ready_order.size());
+    if (order) std::copy(r->ready_order.begin(), r->ready_order.end(), order);
+    return DDP_OK;
+}
+
+int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched)
+{
+    if (!r || !n_launched) return fail(DDP_ERR_INVALID, "NULL argument");
+    *n_launched = r->next;
+    return DDP_OK;
+}
+
+int ddp_set_timing(ddp_reducer *r, int32_t enable)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device");
+    r->timing = enable != 0;
+    if (r->timing) r->timed_bucket.clear();
+    return DDP_OK;
+}
+
+int ddp_get_timings(const ddp_reducer *r, int32_t *buckets, float *ms, int32_t capacity, int32_t *n)
+{
+    if (!r || !n || capacity < 0) return fail(DDP_ERR_INVALID, "bad argument");
+    *n = int32_t(r->timed_bucket.size());
+    const int32_t m = std::min(capacity, *n);
+    for (int32_t i = 0; i < m; ++i) {
+        if (buckets) buckets[i] = r->timed_bucket[i];
+        if (ms) {
+            hipError_t e = hipEventElapsedTime(&ms[i], r->t0[i], r->t1[i]);
+            if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+        }
+    }
+    return DDP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,217 @@
+/* ddp.h — bucketed gradient reduction for data-parallel training, MI355X (gfx950).
+ *
+ * C ABI of libddp.so. Plain pointers and sizes only; every function returns
+ * an int status (DDP_OK = 0, negative on error, text in ddp_last_error())
+ * unless stated otherwise, and never throws.
+ *
+ * Sources (cited by tag and section):
+ *   [DDP-ch17]    "PyTorch 训练框架内核深度解析", chapter 17
+ *                 "DDP：环形 AllReduce 与梯度桶" (yangyitao.com)
+ *   [L15]         CMU 11-868 lecture 15 notes, "分布式训练（二）：PyTorch DDP 的
+ *                 设计与实现" (semidirectx.com)
+ *   [MegatronDDP] "Megatron DDP：连续 buffer 与通信 overlap" (llm-infra-atlas)
+ *   [PTD-notes]   notes on "PyTorch Distributed: Experiences on Accelerating
+ *                 Data Parallel Training" (arcsin2.cloud)
+ *
+ * On one GPU the W data-parallel replicas are W gradient buffers resident in
+ * HBM, so a bucket "all-reduce" is one streaming kernel: it reads the bucket
+ * from all W replicas, scales by 1/W, sums in the ring all-reduce's order and
+ * writes the identical mean back to all W replicas' flat buffers.
+ *
+ * Memory ownership: the caller allocates and owns every device buffer
+ * (gradients, flat buffers, workspace) and both streams; they must stay
+ * valid until ddp_reducer_destroy returns. The library copies the plan and
+ * the pointer tables into its own host memory at creation and writes its
+ * device tables into the caller's workspace; it allocates no device memory.
+ *
+ * Threading: a reducer is used from one thread at a time (hooks fire from
+ * one thread, [DDP-ch17 §17.12]). ddp_last_error() text is per thread.
+ */
+#ifndef DDP_H
+#define DDP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DDP_OK = 0,
+    DDP_ERR_INVALID = -1,        /* bad argument or inconsistent plan                                */
+    DDP_ERR_ALREADY_READY = -2,  /* a gradient marked ready twice in one backward [DDP-ch17 §17.16]  */
+    DDP_ERR_UNFINISHED = -3,     /* new iteration while buckets of the last one never launched
+                                    [DDP-ch17 §17.6; L15 §4.2]                                      */
+    DDP_ERR_NOT_READY = -4,      /* finish while some buckets still wait for gradients             */
+    DDP_ERR_ORDER = -5,          /* explicit reduce of a bucket whose gradients are not all ready   */
+    DDP_ERR_HIP = -6,            /* a HIP runtime call failed (its text is in ddp_last_error)        */
+    DDP_ERR_HOOK = -7            /* a registered communication hook returned non-zero               */
+};
+
+enum {
+    DDP_ORDER_REVERSE = 0,          /* parameters P-1 .. 0: reverse registration order
+                                       [DDP-ch17 §17.3.1; L15 §2.2]                                  */
+    DDP_ORDER_GIVEN = 1,            /* the caller's order, e.g. the ready order recorded in an
+                                       earlier iteration (rebuild) [DDP-ch17 §17.13]                 */
+    DDP_ORDER_FWD_THEN_REVERSE = 2  /* form buckets in forward order, then reverse the list of
+                                       buckets (layout without a rebuild) [DDP-ch17 §17.13]          */
+};
+
+enum {
+    DDP_IN_F32_COPY = 0,        /* fp32 per-parameter gradients, copied into the flat buffer while
+                                   being reduced [DDP-ch17 §17.5, §17.12]                           */
+    DDP_IN_F32_VIEW = 1,        /* the gradients already live in the flat buffer (bucket views),
+                                   reduced in place [DDP-ch17 §17.5]                               */
+    DDP_IN_BF16_ACCUM_F32 = 2   /* bf16 weight gradients accumulated into the fp32 flat main_grad
+                                   buffer, then reduced in place [MegatronDDP §1]                   */
+};
+
+/* ---------------------------------------------------------------------------
+ * ddp_plan_buckets — assign gradients to buckets. Host only, no device.
+ *
+ * Walks the parameters in the order the mode selects, appends each one to
+ * the open bucket and seals the bucket as soon as its bytes reach the cap
+ * (so a bucket may exceed it) [DDP-ch17 §17.2; L15 §2.2, §8 exercise 3].
+ * The first bucket formed uses first_cap_bytes (1 MiB after a rebuild in
+ * PyTorch), every later one cap_bytes (25 MiB by default) [DDP-ch17 §17.2,
+ * §17.13]. cap_bytes = INT64_MAX gives one bucket (PyTorch's first
+ * iteration) and 0 one bucket per gradient [L15 §3.2]. Megatron's bucket size
+ * max(40 MB, 1 MB x DP) is passed as cap = first cap [MegatronDDP §1].
+ *
+ * Buckets are numbered in launch order. Inside a bucket, gradients are laid
+ * out back to back in append order (bytes, no padding); buckets follow one
+ * another in the flat buffer, bucket 0 first.
+ *
+ *   n_params          P >= 0
+ *   param_bytes       [P] bytes of each gradient (>= 0; multiples of 4 for the reducer)
+ *   order             [P] permutation of 0..P-1, read only for DDP_ORDER_GIVEN (may be NULL otherwise)
+ *   order_mode        DDP_ORDER_*
+ *   cap_bytes, first_cap_bytes   >= 0
+ * Outputs (caller-allocated, each may be NULL if not wanted):
+ *   bucket_of         [P] bucket index of each gradient
+ *   offset_in_bucket  [P] byte offset of each gradient inside its bucket
+ *   bucket_params     [P] gradient indices bucket by bucket, append order
+ *   bucket_nparams    [P] gradients per bucket (first *n_buckets entries used)
+ *   bucket_bytes      [P] bytes per bucket (first *n_buckets entries used)
+ *   n_buckets         number of buckets (required)
+ * Errors: DDP_ERR_INVALID for negative sizes or caps, a missing required
+ * array, or an order that is not a permutation.
+ * ------------------------------------------------------------------------- */
+int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t *order, int32_t order_mode,
+                     int64_t cap_bytes, int64_t first_cap_bytes, int32_t *bucket_of, int64_t *offset_in_bucket,
+                     int32_t *bucket_params, int32_t *bucket_nparams, int64_t *bucket_bytes, int32_t *n_buckets);
+
+/* ---------------------------------------------------------------------------
+ * Reducer: one model's gradients over W replicas, reduced bucket by bucket.
+ * ------------------------------------------------------------------------- */
+typedef struct ddp_reducer ddp_reducer;   /* opaque, owned by the library */
+
+typedef struct {
+    int32_t world;                     /* W >= 1 replicas                                           */
+    int32_t n_params;                  /* P >= 0                                                    */
+    const int64_t *param_numel;        /* [P] elements per gradient                                 */
+    const int32_t *bucket_of;          /* [P] a plan (e.g. from ddp_plan_buckets)                   */
+    const int64_t *offset_in_bucket;   /* [P] bytes, multiples of 4; each bucket's gradients must
+                                          tile [0, bucket bytes) exactly                            */
+    int32_t n_buckets;                 /* every bucket must hold at least one gradient              */
+    int32_t input_mode;                /* DDP_IN_*                                                  */
+    const void *const *grads;          /* [W*P] device pointers, entry w*P + p = replica w's
+                                          gradient p: fp32 (COPY) or bf16 (BF16_ACCUM); unused and
+                                          may be NULL for VIEW                                      */
+    float *const *flat;                /* [W] device pointers: replica w's flat fp32 buffer of
+                                          sum(bucket bytes) bytes, laid out by the plan (the bucket
+                                          buffer, or main_grad in BF16_ACCUM mode). NULL: no device
+                                          is used and a communication hook must be registered
+                                          before any bucket launches                               */
+    void *workspace;                   /* device memory of ddp_workspace_bytes() bytes, 256-B
+                                          aligned; unused when flat is NULL                         */
+    size_t workspace_bytes;
+    void *compute_stream;              /* hipStream_t on which gradients are produced               */
+    void *comm_stream;                 /* hipStream_t on which bucket reductions run (a side
+                                          stream that overlaps backward [PTD-notes §2.3])           */
+} ddp_reducer_desc;
+
+/* Device workspace the reducer needs for its tables (segments, tiles,
+ * pointers). Returns 0 and sets ddp_last_error() if the desc is invalid. */
+size_t ddp_workspace_bytes(const ddp_reducer_desc *desc);
+
+/* Validates the desc, copies the plan, builds and uploads the device tables
+ * (synchronously) and leaves the reducer ready for its first backward.
+ * *out is set only on success. */
+int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out);
+
+/* Releases host state and events; the caller's buffers are untouched. NULL is a no-op. */
+int ddp_reducer_destroy(ddp_reducer *r);
+
+/* Resets every bucket's pending count and the per-iteration ready set before
+ * a backward [DDP-ch17 §17.12, §17.16]. DDP_ERR_UNFINISHED if gradients were
+ * marked since the last reset but the iteration was never finished; the
+ * message lists the gradients that got none, ascending [DDP-ch17 §17.6]. */
+int ddp_prepare_for_backward(ddp_reducer *r);
+
+/* The gradient-ready hook for gradient `param` [DDP-ch17 §17.3, §17.12; L15
+ * §2.3; MegatronDDP §2]: decrements its bucket's pending count, then launches
+ * buckets strictly by index, from the first unlaunched one, for as long as
+ * their counts are zero. A launch makes the comm stream wait for the work
+ * queued so far on the compute stream, then runs the registered hook or, by
+ * default, the bucket reduction on the comm stream. May launch 0..B buckets.
+ * Errors: DDP_ERR_INVALID (index out of range), DDP_ERR_ALREADY_READY,
+ * DDP_ERR_HIP, DDP_ERR_HOOK; a launch that failed still counts as issued. */
+int ddp_mark_ready(ddp_reducer *r, int32_t param);
+
+/* The default communication hook: enqueues the reduction of `bucket` on
+ * `stream` (a hipStream_t; NULL is the null stream) without waiting for any
+ * other stream. Callable from a registered hook, or on its own for timing.
+ * During an iteration it refuses (DDP_ERR_ORDER) a bucket not yet launched by
+ * ddp_mark_ready, whose gradients may still be in flight.
+ *
+ * Per element e of the bucket (n elements, chunk length q = ceil(n/W),
+ * chunk c = e / q): t_w = x_w[e] * fp32(1/W) (COPY, VIEW) or
+ * (main_w[e] + fp32(wgrad_w[e])) * fp32(1/W) (BF16_ACCUM);
+ * acc = t_c, then acc += t_{c+1}, ..., t_{c+W-1} (indices mod W), each an
+ * fp32 add rounded to nearest even: the value the ring reduce-scatter leaves
+ * for chunk c [DDP-ch17 §17.4, §17.9; MegatronDDP §3]. acc is written to
+ * element e of all W flat buffers (the all-gather). */
+int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
+
+/* End of backward [DDP-ch17 §17.41; MegatronDDP §5]: checks that every bucket
+ * launched (DDP_ERR_NOT_READY otherwise, listing the gradients not marked
+ * ready), then makes the compute stream wait for the comm stream; with
+ * host_blocking != 0 the host also waits for the reductions to complete. */
+int ddp_finish(ddp_reducer *r, int32_t host_blocking);
+
+/* Replaces the default hook [DDP-ch17 §17.9, §17.20; L15 §2.2]: fn(ctx, b)
+ * is called for each bucket launch, in launch order, after the comm stream
+ * was made to wait on the compute stream. fn = NULL restores the default. */
+typedef int (*ddp_comm_hook_fn)(void *ctx, int32_t bucket);
+int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx);
+
+/* Plan introspection (bucket sizes and members, [DDP-ch17 §17.39]). */
+int ddp_get_bucket(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t *flat_offset_bytes,
+                   int32_t *n_params);
+/* params: [n_params of that bucket], in flat-buffer order */
+int ddp_get_bucket_params(const ddp_reducer *r, int32_t bucket, int32_t *params);
+/* Gradients in the order they were marked ready since the last reset, the
+ * input of a rebuild with DDP_ORDER_GIVEN [DDP-ch17 §17.13]. order: [P]. */
+int ddp_get_ready_order(const ddp_reducer *r, int32_t *order, int32_t *n);
+/* Buckets launched since the last reset. */
+int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched);
+
+/* Per-launch timing: while enabled, each default bucket reduction is
+ * bracketed by two HIP events on the stream it runs on. Enabling (again)
+ * starts a new record list; the events are kept and reused.
+ * ddp_get_timings copies up to `capacity` records (launch order) of the
+ * launches since timing was last enabled: the bucket index and the kernel's
+ * duration in ms. The caller must first wait for those launches to complete
+ * (e.g. ddp_finish with host_blocking). *n = number of records. */
+int ddp_set_timing(ddp_reducer *r, int32_t enable);
+int ddp_get_timings(const ddp_reducer *r, int32_t *buckets, float *ms, int32_t capacity, int32_t *n);
+
+/* Text of the last error on this thread ("" if none). Never NULL. */
+const char *ddp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DDP_H */

@@ -1,0 +1,105 @@
+"""Device-resident synthetic gradient sets for a workload (torch allocates,
+the generator in synth_device.hip fills). Inputs only: nothing here reduces.
+
+Layout per replica w:
+  * gradient tensors (fp32 grads, or bf16 wgrads in the Megatron mode) live in
+    one allocation per replica, each tensor starting on a 256-byte boundary --
+    a stand-in for separately allocated .grad tensors;
+  * one flat fp32 buffer of the plan's total size: the bucket buffer, and in
+    the view / bf16-accumulate modes also the input (gradients already in
+    place, or the fp32 main_grad).
+The flat position of gradient p comes from the caller's bucket plan.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from . import fill_dev, key, scale_for
+from .workloads import (IN_BF16_ACCUM_F32, IN_F32_COPY, IN_F32_VIEW, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD,
+                        Workload)
+
+ALIGN = 256
+SENTINEL = -1   # 0xFFFFFFFF: a NaN pattern the reduction never produces from finite inputs
+
+
+class DeviceInputs:
+    def __init__(self, wl: Workload, flat_offset_elems: Sequence[int], total_elems: int, device: str = "cuda",
+                 seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0):
+        """misalign: bytes added to the start of every other gradient tensor
+        (to exercise unaligned sources); flat_shift: elements the flat
+        buffers start past their allocation (to exercise unaligned outputs)."""
+        import torch
+
+        self.wl = wl
+        self.W = W = wl.world
+        self.numel = wl.numel
+        self.P = P = len(self.numel)
+        self.seed = wl.seed if seed is None else seed
+        self.flat_offset = list(int(x) for x in flat_offset_elems)
+        self.total = int(total_elems)
+        self.mode = wl.input_mode
+        self.dist = wl.dist
+        self.scale = scale_for(wl.dist, wl.sigma)
+        esz = 2 if self.mode == IN_BF16_ACCUM_F32 else 4
+        self.esz = esz
+        self.grad_off: List[int] = []      # byte offsets inside each replica's gradient allocation
+        cur = 0
+        for p, n in enumerate(self.numel):
+            shift = misalign if p % 2 else 0
+            self.grad_off.append(cur + shift)
+            cur += (n * esz + shift + ALIGN - 1) // ALIGN * ALIGN
+        self.grad_bytes = max(cur, ALIGN)
+        self.grads = []
+        if self.mode != IN_F32_VIEW:
+            self.grads = [torch.empty(self.grad_bytes, dtype=torch.uint8, device=device) for _ in range(W)]
+        self.flat_shift = flat_shift
+        self._flat_alloc = [torch.empty(max(self.total, 1) + flat_shift, dtype=torch.float32, device=device)
+                            for _ in range(W)]
+        self.flat = [a[flat_shift:] for a in self._flat_alloc]
+        self.refill()
+
+    # pointers -------------------------------------------------------------
+    def grad_ptrs(self) -> Optional[List[List[int]]]:
+        if self.mode == IN_F32_VIEW:
+            return None
+        return [[g.data_ptr() + off for off in self.grad_off] for g in self.grads]
+
+    def flat_ptrs(self) -> List[int]:
+        return [f.data_ptr() for f in self.flat]
+
+    # generation -----------------------------------------------------------
+    def input_stream(self) -> int:
+        return STREAM_WGRAD if self.mode == IN_BF16_ACCUM_F32 else STREAM_GRAD
+
+    def refill(self) -> None:
+        """(Re)writes every input from the generator; flat buffers that are
+        pure outputs get the sentinel pattern."""
+        import torch
+
+        W, P = self.W, self.P
+        if self.mode == IN_F32_COPY:
+            for f in self.flat:
+                f.view(torch.int32).fill_(SENTINEL)
+        if self.mode != IN_F32_VIEW:
+            ents = []
+            for w in range(W):
+                base = self.grads[w].data_ptr()
+                for p in range(P):
+                    if self.numel[p]:
+                        ents.append((base + self.grad_off[p], self.numel[p], key(self.seed, self.input_stream(), w, p)))
+            fill_dev(ents, self.dist, self.scale, bf16=self.mode == IN_BF16_ACCUM_F32)
+        if self.mode in (IN_F32_VIEW, IN_BF16_ACCUM_F32):
+            stream = STREAM_GRAD if self.mode == IN_F32_VIEW else STREAM_MAIN
+            ents = []
+            for w in range(W):
+                base = self.flat[w].data_ptr()
+                for p in range(P):
+                    if self.numel[p]:
+                        ents.append((base + 4 * self.flat_offset[p], self.numel[p], key(self.seed, stream, w, p)))
+            fill_dev(ents, self.dist, self.scale, bf16=False)
+        torch.cuda.synchronize()
+
+    def nbytes(self) -> int:
+        return sum(g.numel() for g in self.grads) + 4 * sum(f.numel() for f in self.flat)

@@ -1,0 +1,279 @@
+"""libddp through its C ABI on the CPU: exported symbols, the bucket plan
+against the oracle, and the reducer's state machine driven through a
+recording communication hook (no device buffers, so no GPU is touched)."""
+import os
+import random
+import re
+import sys
+
+import numpy as np
+import pytest
+
+import bucketed_gradient_all_amd as ddp
+from conftest import ROOT, golden
+from oracle.plan import plan_buckets
+from oracle.reducer_model import ReducerModel, ModelError
+
+INF = sys.maxsize
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(ddp.LIB_PATH):
+        ddp.build()
+    ddp.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ddp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    import ctypes
+    names = header_functions()
+    assert len(names) >= 16
+    L = ctypes.CDLL(ddp.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert missing == []
+
+
+def test_library_has_gfx950_code_object():
+    data = open(ddp.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+# ---------------------------------------------------------------- planning
+def _rand_case(rng):
+    P = rng.randint(0, 50)
+    pb = [rng.choice([0, 4, 16, 64, 4096, rng.randint(0, 9000) * 4]) for _ in range(P)]
+    cap = rng.choice([0, 4, 64, 1000, 20000, INF])
+    first = rng.choice([0, 16, 1024, cap])
+    return pb, cap, first
+
+
+@pytest.mark.parametrize("seed", range(80))
+def test_plan_matches_oracle(seed):
+    rng = random.Random(seed)
+    pb, cap, first = _rand_case(rng)
+    P = len(pb)
+    for mode in (ddp.DDP_ORDER_REVERSE, ddp.DDP_ORDER_FWD_THEN_REVERSE, ddp.DDP_ORDER_GIVEN):
+        order = None
+        if mode == ddp.DDP_ORDER_GIVEN:
+            order = list(range(P))
+            rng.shuffle(order)
+        got = ddp.ddp_plan_buckets(pb, mode, cap, first, order)
+        want = plan_buckets(pb, mode, order=order, cap=cap, first_cap=first)
+        assert got.buckets() == want.buckets
+        assert list(got.bucket_bytes) == want.bucket_bytes
+        assert list(got.bucket_of) == want.bucket_of
+        assert list(got.offset_in_bucket) == want.offset_in_bucket
+
+
+def test_plan_page_examples():
+    g = golden("ddp_ch17_linear12_buckets.json")
+    pb = [1024 * 1024 * 4, 1024 * 4] * 12
+    p = ddp.ddp_plan_buckets(pb, ddp.DDP_ORDER_REVERSE, g["cap_bytes"], g["first_cap_bytes"])
+    assert list(p.bucket_bytes) == g["rebuilt_reverse_order_bucket_bytes"]
+    p = ddp.ddp_plan_buckets(pb, ddp.DDP_ORDER_FWD_THEN_REVERSE, g["cap_bytes"], g["first_cap_bytes"])
+    assert list(p.bucket_bytes) == g["find_unused_fwd_then_reverse_bucket_bytes"]
+    p = ddp.ddp_plan_buckets(pb, ddp.DDP_ORDER_REVERSE, INF, INF)
+    assert list(p.bucket_bytes) == [50380800]
+    g3 = golden("l15_exercise3_buckets.json")
+    p = ddp.ddp_plan_buckets(g3["param_sizes_mb"], ddp.DDP_ORDER_REVERSE, g3["cap_mb"], g3["cap_mb"])
+    assert p.buckets() == g3["buckets"]
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_plan_buckets([4, -4])
+    assert e.value.code == ddp.DDP_ERR_INVALID
+    with pytest.raises(ddp.DDPError):
+        ddp.ddp_plan_buckets([4, 4], ddp.DDP_ORDER_GIVEN, 8, 8, order=[0, 0])
+    with pytest.raises(ddp.DDPError):
+        ddp.ddp_plan_buckets([4, 4], 7, 8, 8)
+    with pytest.raises(ddp.DDPError):
+        ddp.ddp_plan_buckets([4, 4], ddp.DDP_ORDER_REVERSE, -1, 8)
+
+
+# ----------------------------------------------------------- state machine
+def host_reducer(pb_elems, cap, first, W=2, mode=ddp.DDP_ORDER_REVERSE, order=None):
+    pb = [4 * n for n in pb_elems]
+    plan = ddp.ddp_plan_buckets(pb, mode, cap, first, order)
+    desc = ddp.Desc(W, pb_elems, plan.bucket_of, plan.offset_in_bucket, plan.n_buckets)
+    r = ddp.ddp_reducer_create(desc)
+    log = []
+    ddp.ddp_register_comm_hook(r, lambda b: log.append(b) or 0)
+    return r, plan, log
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_state_machine_matches_oracle(seed):
+    rng = random.Random(seed)
+    P = rng.randint(1, 30)
+    numel = [rng.randint(0, 40) for _ in range(P)]
+    r, plan, log = host_reducer(numel, rng.choice([0, 16, 64, 400, INF]), rng.choice([16, 64]))
+    model = ReducerModel(plan.buckets(), P)
+    for it in range(3):
+        order = list(range(P))
+        rng.shuffle(order)
+        skip = rng.random() < 0.3 and P > 1
+        marked = order[:-1] if skip else order
+        for p in marked:
+            before = len(log)
+            ddp.ddp_mark_ready(r, p)
+            assert log[before:] == model.mark_ready(p)
+        assert ddp.ddp_get_ready_order(r) == marked
+        assert ddp.ddp_get_launched(r) == model.next_bucket
+        if skip:
+            with pytest.raises(ddp.DDPError) as e:
+                ddp.ddp_finish(r)
+            assert e.value.code == ddp.DDP_ERR_NOT_READY
+            with pytest.raises(ModelError):
+                model.finish()
+            with pytest.raises(ddp.DDPError) as e:
+                ddp.ddp_prepare_for_backward(r)
+            assert e.value.code == ddp.DDP_ERR_UNFINISHED
+            missing = sorted(set(range(P)) - set(marked))
+            assert e.value.msg.endswith(" ".join(map(str, missing)))
+            # finish the iteration so the next one can start
+            ddp.ddp_mark_ready(r, order[-1])
+            log_tail = model.mark_ready(order[-1])
+            assert log[-len(log_tail):] == log_tail if log_tail else True
+        ddp.ddp_finish(r)
+        model.finish()
+        ddp.ddp_prepare_for_backward(r)
+        model.prepare_for_backward()
+    assert log == model.launched
+    ddp.ddp_reducer_destroy(r)
+
+
+def test_double_mark_and_index_errors():
+    r, plan, log = host_reducer([4, 4, 4], 16, 16)
+    ddp.ddp_mark_ready(r, 2)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, 2)
+    assert e.value.code == ddp.DDP_ERR_ALREADY_READY
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, 3)
+    assert e.value.code == ddp.DDP_ERR_INVALID
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, -1)
+    assert e.value.code == ddp.DDP_ERR_INVALID
+
+
+def test_unused_parameters_reported_at_next_prepare():
+    """Two parameters of an unused branch never get a gradient; the next
+    iteration's prepare fails naming exactly those, ascending."""
+    r, plan, log = host_reducer([4, 4, 4, 4], 16, 16)
+    for p in (1, 0):
+        ddp.ddp_mark_ready(r, p)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_prepare_for_backward(r)
+    assert e.value.code == ddp.DDP_ERR_UNFINISHED
+    assert e.value.msg.endswith(": 2 3")
+
+
+def test_hook_error_and_missing_device():
+    r, plan, log = host_reducer([4, 4], 16, 16)
+    ddp.ddp_register_comm_hook(r, lambda b: 5)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, 1)
+        ddp.ddp_mark_ready(r, 0)
+    assert e.value.code == ddp.DDP_ERR_HOOK
+    r2, _, _ = host_reducer([4, 4], 0, 0)
+    ddp.ddp_register_comm_hook(r2, None)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r2, 1)      # cap 0: bucket 0 = {1} launches at once
+    assert e.value.code == ddp.DDP_ERR_INVALID
+
+
+def test_explicit_reduce_of_unready_bucket_is_refused():
+    r, plan, log = host_reducer([2, 2, 2, 2], 16, 16)   # 8-byte gradients: buckets [[3,2],[1,0]]
+    assert plan.buckets() == [[3, 2], [1, 0]]
+    ddp.ddp_mark_ready(r, 3)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_bucket_reduce(r, 1, 0)
+    assert e.value.code == ddp.DDP_ERR_ORDER
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_bucket_reduce(r, 0, 0)
+    assert e.value.code == ddp.DDP_ERR_ORDER
+    ddp.ddp_mark_ready(r, 2)
+    # bucket 0 is launched now; without device buffers the default reduction has nothing to run on
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_bucket_reduce(r, 0, 0)
+    assert e.value.code == ddp.DDP_ERR_INVALID
+
+
+def test_rebuild_from_recorded_ready_order():
+    """Iteration 1 with one bucket records the real ready order; the rebuilt
+    plan uses it with a small first cap [DDP-ch17 §17.13]."""
+    numel = [1024 * 1024, 1024] * 12
+    r, plan, log = host_reducer(numel, INF, INF)
+    assert plan.n_buckets == 1
+    real = list(range(23, -1, -1))
+    real[0], real[1] = real[1], real[0]          # weight before bias in the last layer
+    for p in real:
+        ddp.ddp_mark_ready(r, p)
+    ddp.ddp_finish(r)
+    order = ddp.ddp_get_ready_order(r)
+    assert order == real
+    rebuilt = ddp.ddp_plan_buckets([4 * n for n in numel], ddp.DDP_ORDER_GIVEN, 25 << 20, 1 << 20, order)
+    assert list(rebuilt.bucket_bytes) == [4194304, 29392896, 16793600]
+    assert rebuilt.buckets()[0] == [22]
+
+
+def test_introspection():
+    r, plan, log = host_reducer([10, 20, 30, 0, 40], 160, 100)
+    for b in range(plan.n_buckets):
+        nbytes, off, n = ddp.ddp_get_bucket(r, b)
+        assert nbytes == plan.bucket_bytes[b]
+        assert off == int(sum(plan.bucket_bytes[:b]))
+        members = ddp.ddp_get_bucket_params(r, b)
+        assert sorted(members) == sorted(plan.buckets()[b])
+        offs = [int(plan.offset_in_bucket[p]) for p in members]
+        assert offs == sorted(offs)
+    with pytest.raises(ddp.DDPError):
+        ddp.ddp_get_bucket(r, plan.n_buckets)
+
+
+def _desc(numel, bucket_of, offsets, nb, W=2, mode=ddp.DDP_IN_F32_COPY):
+    return ddp.Desc(W, numel, bucket_of, offsets, nb, mode)
+
+
+@pytest.mark.parametrize("case", [
+    dict(numel=[4, 4], bucket_of=[0, 0], offsets=[0, 8], nb=1),        # gap
+    dict(numel=[4, 4], bucket_of=[0, 0], offsets=[0, 0], nb=1),        # overlap
+    dict(numel=[4, 4], bucket_of=[0, 2], offsets=[0, 0], nb=2),        # bucket out of range
+    dict(numel=[4, 4], bucket_of=[0, 0], offsets=[0, 16], nb=2),       # empty bucket 1
+    dict(numel=[4, 4], bucket_of=[0, 0], offsets=[0, 18], nb=1),       # unaligned offset
+    dict(numel=[-4, 4], bucket_of=[0, 0], offsets=[0, 0], nb=1),       # negative size
+    dict(numel=[4], bucket_of=[0], offsets=[0], nb=1, W=0),            # no replicas
+    dict(numel=[4], bucket_of=[0], offsets=[0], nb=1, mode=9),         # unknown mode
+])
+def test_invalid_descs_are_rejected(case):
+    d = _desc(**case)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_reducer_create(d)
+    assert e.value.code == ddp.DDP_ERR_INVALID
+    with pytest.raises(ddp.DDPError):
+        ddp.ddp_workspace_bytes(d)
+
+
+def test_workspace_size_grows_with_the_model():
+    small = ddp.ddp_plan_buckets([4000] * 4, ddp.DDP_ORDER_REVERSE, 8000, 8000)
+    big = ddp.ddp_plan_buckets([400000] * 40, ddp.DDP_ORDER_REVERSE, 8000, 8000)
+    ds = _desc([1000] * 4, small.bucket_of, small.offset_in_bucket, small.n_buckets, W=8)
+    db = _desc([100000] * 40, big.bucket_of, big.offset_in_bucket, big.n_buckets, W=8)
+    a, b = ddp.ddp_workspace_bytes(ds), ddp.ddp_workspace_bytes(db)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+
+
+def test_create_with_device_buffers_needs_a_workspace():
+    plan = ddp.ddp_plan_buckets([16, 16], ddp.DDP_ORDER_REVERSE, 16, 16)
+    d = ddp.Desc(1, [4, 4], plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, ddp.DDP_IN_F32_COPY,
+                 grads=[[4096, 8192]], flat=[16384])
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_reducer_create(d)
+    assert e.value.code == ddp.DDP_ERR_INVALID and "workspace" in e.value.msg
