@@ -65,7 +65,7 @@ def measured_traffic(workload: str):
 
 
 class Session:
-    def __init__(self, wl):
+    def __init__(self, wl, arena: bool = False):
         import numpy as np
         import torch
 
@@ -81,21 +81,20 @@ class Session:
         self.total = sum(bb) // 4
         self.bucket_bytes = bb
         t0 = time.perf_counter()
-        self.inputs = DeviceInputs(wl, flat_off, self.total)
+        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena)
         log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
         self.compute = torch.cuda.Stream()
         self.comm = torch.cuda.Stream()
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
                                   self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream)
-        self.order = list(range(len(wl.numel) - 1, -1, -1))
-        self.members = self.plan.buckets()
+        self.order = np.arange(len(wl.numel) - 1, -1, -1, dtype=np.int32)
+        self.members = [np.asarray(m, np.int32) for m in self.plan.buckets()]
 
     def step(self, backward_us: float = 0.0, serial: bool = False):
         ddp = self.ddp
         ddp.ddp_prepare_for_backward(self.r)
         if backward_us <= 0:
-            for p in self.order:
-                ddp.ddp_mark_ready(self.r, p)
+            ddp.ddp_mark_ready_many(self.r, self.order)
         else:
             import synth
             tot = float(sum(self.bucket_bytes)) or 1.0
@@ -105,17 +104,20 @@ class Session:
             for b, members in enumerate(self.members):
                 if not serial:
                     synth.spin_dev(backward_us * self.bucket_bytes[b] / tot, cs)
-                for p in members:
-                    ddp.ddp_mark_ready(self.r, p)
+                ddp.ddp_mark_ready_many(self.r, members)
         ddp.ddp_finish(self.r, host_blocking=False)
 
     def timed(self, steps: int, **kw):
         torch = self.torch
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        issue = 0.0
         for _ in range(steps):
+            ti = time.perf_counter()
             self.step(**kw)
+            issue += time.perf_counter() - ti
         torch.cuda.synchronize()
+        self.last_issue_s = issue / max(steps, 1)
         return time.perf_counter() - t0
 
 
@@ -204,8 +206,8 @@ def cpu_baseline(wl, session, target_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="resnet50",
                     help="tiny | resnet50 | bert_large | megatron_llama1b | sweep_w{W}_cap{MiB}")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
@@ -258,11 +260,17 @@ def main():
     for _ in range(args.warmup):
         s.step()
     torch.cuda.synchronize()
-    ddp.ddp_set_timing(s.r, True)
     log(f"[bench] timing {args.steps} steps")
     elapsed = s.timed(args.steps)
+    issue_plain = s.last_issue_s
+    # the same steps again with HIP events around every bucket launch on the
+    # comm stream: per-launch kernel durations for the roofline
+    ddp.ddp_set_timing(s.r, True)
+    ev_elapsed = s.timed(args.steps)
     buckets, ms = ddp.ddp_get_timings(s.r)
     ddp.ddp_set_timing(s.r, False)
+    log(f"[bench] step {elapsed / args.steps * 1e3:.3f} ms (host issue {issue_plain * 1e3:.3f} ms); "
+        f"{ev_elapsed / args.steps * 1e3:.3f} ms with per-launch events")
     step_s = elapsed / args.steps
     value = bytes_per_step / step_s / 1e9
     kernel_s = float(ms.sum()) / 1e3

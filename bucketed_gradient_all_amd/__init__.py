@@ -97,6 +97,7 @@ def lib():
             "ddp_reducer_destroy": [P],
             "ddp_prepare_for_backward": [P],
             "ddp_mark_ready": [P, I32],
+            "ddp_mark_ready_many": [P, P, I32, P],
             "ddp_bucket_reduce": [P, I32, P],
             "ddp_finish": [P, I32],
             "ddp_register_comm_hook": [P, HOOK_FN, P],
@@ -235,6 +236,18 @@ def ddp_prepare_for_backward(r: Reducer) -> None:
 
 def ddp_mark_ready(r: Reducer, param: int) -> None:
     _check(lib().ddp_mark_ready(r.handle, param))
+
+
+def ddp_mark_ready_many(r: Reducer, params) -> int:
+    """Marks params in order; returns how many were marked (all, unless it raises)."""
+    arr = np.ascontiguousarray(params, dtype=np.int32)
+    done = ctypes.c_int32()
+    rc = lib().ddp_mark_ready_many(r.handle, arr.ctypes.data, arr.size, ctypes.byref(done))
+    if rc < 0:
+        err = DDPError(rc, ddp_last_error())
+        err.n_done = done.value
+        raise err
+    return done.value
 
 
 def ddp_bucket_reduce(r: Reducer, bucket: int, stream: int) -> None:

@@ -34,8 +34,8 @@ struct DeviceSeg {
     int32_t param;   // source gradient (COPY, BF16_ACCUM); -1 for VIEW
     int32_t chunk;   // ring chunk c: the fold starts at replica c
     int32_t tile0;   // first tile of this segment
-    int32_t head;    // scalar elements before the 16-byte aligned body, or -1:
-                     // the segment is processed one element per lane
+    int32_t head;    // scalar elements (0..63) before the aligned vector body,
+                     // or -1: the segment is processed one element per lane
 };
 
 struct KernelTables {

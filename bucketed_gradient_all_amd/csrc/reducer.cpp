@@ -272,12 +272,18 @@ int enqueue_reduce(ddp_reducer *r, int32_t b, hipStream_t s)
 // All-reduce of one bucket as issued by the reducer: the comm stream first
 // waits for everything queued on the compute stream (the bucket's gradients
 // were produced there), then the hook or the default reduction runs on it
-// [PTD-notes §2.3; MegatronDDP §3].
+// [PTD-notes §2.3; MegatronDDP §3]. When the compute stream has already
+// drained, every gradient it produced is complete and visible, so the
+// cross-stream event (a few microseconds of queue latency per bucket) is
+// skipped.
 int launch_bucket(ddp_reducer *r, int32_t b)
 {
     if (r->device && r->compute != r->comm) {
-        hipError_t e = hipEventRecord(r->ev_ready, r->compute);
-        if (e == hipSuccess) e = hipStreamWaitEvent(r->comm, r->ev_ready, 0);
+        hipError_t e = hipStreamQuery(r->compute);
+        if (e == hipErrorNotReady) {
+            e = hipEventRecord(r->ev_ready, r->compute);
+            if (e == hipSuccess) e = hipStreamWaitEvent(r->comm, r->ev_ready, 0);
+        }
         if (e != hipSuccess) return hip_fail("stream wait", e);
     }
     if (r->hook) {
@@ -425,14 +431,26 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
             return fail(DDP_ERR_INVALID, "workspace missing, misaligned or smaller than " +
                                              std::to_string(lay.total) + " bytes");
         }
-        // 16-byte vectors where every replica's source and destination allow
-        // them: a segment whose element `head` is 16-byte aligned on the
-        // destination side must be aligned on every source too
-        bool flat_aligned = true;
-        for (int w = 0; w < pv.W; ++w) flat_aligned &= reinterpret_cast<uintptr_t>(desc->flat[w]) % 16 == 0;
+        // Vector body of a segment: it starts at the first element whose
+        // destination address is 256-byte aligned, so every wave's 1 KiB store
+        // run covers whole cache lines (a store run that straddles lines costs
+        // partial-line writes, up to a tenth of the bandwidth); the elements
+        // before it are folded one per lane. This needs every replica's flat
+        // buffer at the same address modulo 256; otherwise the body starts at
+        // 16-byte alignment. Sources must then be 16-byte aligned at the body
+        // start on every replica, else the segment is folded one element per
+        // lane.
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(desc->flat[0]);
+        bool flat_aligned = d0 % 16 == 0, same_phase = true;
+        for (int w = 0; w < pv.W; ++w) {
+            flat_aligned &= reinterpret_cast<uintptr_t>(desc->flat[w]) % 16 == 0;
+            same_phase &= reinterpret_cast<uintptr_t>(desc->flat[w]) % 256 == d0 % 256;
+        }
+        const uintptr_t line = same_phase ? 256 : 16;
         for (DeviceSeg &s : pv.segs) {
             if (!flat_aligned) continue;
-            int64_t head = (4 - (s.flat % 4)) % 4;
+            const uintptr_t a = d0 + 4 * uintptr_t(s.flat);
+            int64_t head = int64_t(((line - a % line) % line) / 4);
             head = std::min(head, s.len);
             bool ok = true;
             if (copy_src) {
@@ -510,6 +528,19 @@ int ddp_mark_ready(ddp_reducer *r, int32_t param)
         const int32_t b = r->next++;
         int rc = launch_bucket(r, b);
         if (rc != DDP_OK) return rc;
+    }
+    return DDP_OK;
+}
+
+int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done)
+{
+    if (n_done) *n_done = 0;
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (n < 0 || (n > 0 && !params)) return fail(DDP_ERR_INVALID, "bad parameter list");
+    for (int32_t i = 0; i < n; ++i) {
+        int rc = ddp_mark_ready(r, params[i]);
+        if (rc != DDP_OK) return rc;
+        if (n_done) *n_done = i + 1;
     }
     return DDP_OK;
 }

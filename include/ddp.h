@@ -154,11 +154,18 @@ int ddp_prepare_for_backward(ddp_reducer *r);
  * §2.3; MegatronDDP §2]: decrements its bucket's pending count, then launches
  * buckets strictly by index, from the first unlaunched one, for as long as
  * their counts are zero. A launch makes the comm stream wait for the work
- * queued so far on the compute stream, then runs the registered hook or, by
- * default, the bucket reduction on the comm stream. May launch 0..B buckets.
+ * queued so far on the compute stream (no wait is enqueued when that stream
+ * has already drained), then runs the registered hook or, by default, the
+ * bucket reduction on the comm stream. May launch 0..B buckets.
  * Errors: DDP_ERR_INVALID (index out of range), DDP_ERR_ALREADY_READY,
  * DDP_ERR_HIP, DDP_ERR_HOOK; a launch that failed still counts as issued. */
 int ddp_mark_ready(ddp_reducer *r, int32_t param);
+
+/* ddp_mark_ready for params[0], params[1], ... in that order, in one call
+ * (gradients that become ready together, e.g. the weight and bias of one
+ * layer). Stops at the first error and returns it; *n_done (may be NULL)
+ * receives how many marks succeeded. */
+int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done);
 
 /* The default communication hook: enqueues the reduction of `bucket` on
  * `stream` (a hipStream_t; NULL is the null stream) without waiting for any

@@ -26,10 +26,13 @@ SENTINEL = -1   # 0xFFFFFFFF: a NaN pattern the reduction never produces from fi
 
 class DeviceInputs:
     def __init__(self, wl: Workload, flat_offset_elems: Sequence[int], total_elems: int, device: str = "cuda",
-                 seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0):
+                 seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0, arena: bool = False):
         """misalign: bytes added to the start of every other gradient tensor
         (to exercise unaligned sources); flat_shift: elements the flat
-        buffers start past their allocation (to exercise unaligned outputs)."""
+        buffers start past their allocation, one value or one per replica (to
+        exercise unaligned outputs);
+        arena: carve every buffer out of one allocation instead of one
+        allocation per buffer."""
         import torch
 
         self.wl = wl
@@ -52,12 +55,26 @@ class DeviceInputs:
             cur += (n * esz + shift + ALIGN - 1) // ALIGN * ALIGN
         self.grad_bytes = max(cur, ALIGN)
         self.grads = []
-        if self.mode != IN_F32_VIEW:
-            self.grads = [torch.empty(self.grad_bytes, dtype=torch.uint8, device=device) for _ in range(W)]
-        self.flat_shift = flat_shift
-        self._flat_alloc = [torch.empty(max(self.total, 1) + flat_shift, dtype=torch.float32, device=device)
-                            for _ in range(W)]
-        self.flat = [a[flat_shift:] for a in self._flat_alloc]
+        shifts = list(flat_shift) if isinstance(flat_shift, (list, tuple)) else [flat_shift] * W
+        self.flat_shift = shifts
+        flat_bytes = (4 * (max(self.total, 1) + max(shifts)) + ALIGN - 1) // ALIGN * ALIGN
+        if arena:
+            gb = self.grad_bytes if self.mode != IN_F32_VIEW else 0
+            self._arena = torch.empty(W * (gb + flat_bytes), dtype=torch.uint8, device=device)
+            base = 0
+            for _ in range(W):
+                if gb:
+                    self.grads.append(self._arena[base:base + gb])
+                    base += gb
+            self._flat_alloc = []
+            for _ in range(W):
+                self._flat_alloc.append(self._arena[base:base + flat_bytes].view(torch.float32))
+                base += flat_bytes
+        else:
+            if self.mode != IN_F32_VIEW:
+                self.grads = [torch.empty(self.grad_bytes, dtype=torch.uint8, device=device) for _ in range(W)]
+            self._flat_alloc = [torch.empty(flat_bytes // 4, dtype=torch.float32, device=device) for _ in range(W)]
+        self.flat = [a[sh:sh + max(self.total, 1)] for a, sh in zip(self._flat_alloc, shifts)]
         self.refill()
 
     # pointers -------------------------------------------------------------

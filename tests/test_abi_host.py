@@ -277,3 +277,23 @@ def test_create_with_device_buffers_needs_a_workspace():
     with pytest.raises(ddp.DDPError) as e:
         ddp.ddp_reducer_create(d)
     assert e.value.code == ddp.DDP_ERR_INVALID and "workspace" in e.value.msg
+
+
+def test_mark_ready_many_equals_single_marks():
+    rng = random.Random(11)
+    numel = [rng.randint(1, 30) for _ in range(20)]
+    r1, plan, log1 = host_reducer(numel, 64, 16)
+    r2, _, log2 = host_reducer(numel, 64, 16)
+    order = list(range(20))
+    rng.shuffle(order)
+    for p in order:
+        ddp.ddp_mark_ready(r1, p)
+    assert ddp.ddp_mark_ready_many(r2, order) == 20
+    assert log1 == log2 == list(range(plan.n_buckets))
+    ddp.ddp_finish(r2)
+    ddp.ddp_prepare_for_backward(r2)
+    # an error stops the batch and reports how far it got
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready_many(r2, [order[0], order[1], order[1], order[2]])
+    assert e.value.code == ddp.DDP_ERR_ALREADY_READY and e.value.n_done == 2
+    assert ddp.ddp_get_ready_order(r2) == order[:2]

@@ -136,7 +136,8 @@ def test_small_random_workloads_bit_exact(W, mode):
 @pytest.mark.parametrize("mode", [0, 2])
 def test_unaligned_sources_and_outputs(mode):
     W = 4
-    for misalign, shift in ((4 if mode == 0 else 2, 0), (0, 1), (4 if mode == 0 else 2, 3)):
+    for misalign, shift in ((4 if mode == 0 else 2, 0), (0, 1), (4 if mode == 0 else 2, 3), (0, 4),
+                            (0, [0, 4, 8, 12]), (0, [0, 64, 0, 64])):
         wl = _small_workload(77, W, mode)
         say(f"case misalign={misalign} flat_shift={shift} mode={mode}")
         run = Run(wl, misalign=misalign, flat_shift=shift)
