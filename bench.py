@@ -90,11 +90,17 @@ class Session:
         self.order = np.arange(len(wl.numel) - 1, -1, -1, dtype=np.int32)
         self.members = [np.asarray(m, np.int32) for m in self.plan.buckets()]
 
-    def step(self, backward_us: float = 0.0, serial: bool = False):
+    def step(self, backward_us: float = 0.0, serial: bool = False, per_bucket: bool = False):
+        """per_bucket: one ready call per bucket, so each bucket is its own
+        launch; otherwise all gradients are marked in one call and the
+        buckets go out as one coalesced launch."""
         ddp = self.ddp
         ddp.ddp_prepare_for_backward(self.r)
-        if backward_us <= 0:
+        if backward_us <= 0 and not per_bucket:
             ddp.ddp_mark_ready_many(self.r, self.order)
+        elif backward_us <= 0:
+            for members in self.members:
+                ddp.ddp_mark_ready_many(self.r, members)
         else:
             import synth
             tot = float(sum(self.bucket_bytes)) or 1.0
@@ -263,32 +269,46 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     elapsed = s.timed(args.steps)
     issue_plain = s.last_issue_s
-    # the same steps again with HIP events around every bucket launch on the
-    # comm stream: per-launch kernel durations for the roofline
+    # the same steps again with HIP events around every launch on the comm
+    # stream: kernel durations for the roofline
     ddp.ddp_set_timing(s.r, True)
     ev_elapsed = s.timed(args.steps)
-    buckets, ms = ddp.ddp_get_timings(s.r)
+    first, count, ms = ddp.ddp_get_timings(s.r)
     ddp.ddp_set_timing(s.r, False)
     log(f"[bench] step {elapsed / args.steps * 1e3:.3f} ms (host issue {issue_plain * 1e3:.3f} ms); "
         f"{ev_elapsed / args.steps * 1e3:.3f} ms with per-launch events")
     step_s = elapsed / args.steps
     value = bytes_per_step / step_s / 1e9
+    W = wl.world
+    per_elem = 10 if wl.input_mode == 2 else 8
+    bucket_alg = [per_elem * W * b // 4 for b in s.bucket_bytes]
+    launch_bytes = [sum(bucket_alg[f:f + c]) for f, c in zip(first, count)]
     kernel_s = float(ms.sum()) / 1e3
     launches = len(ms)
-    per_launch_bytes = bytes_per_step * args.steps / max(launches, 1)
-    achieved = bytes_per_step * args.steps / kernel_s / 1e9 if kernel_s > 0 else 0.0
-    W = wl.world
+    per_launch_bytes = sum(launch_bytes) / max(launches, 1)
+    achieved = sum(launch_bytes) / kernel_s / 1e9 if kernel_s > 0 else 0.0
     bus = sum(2 * (W - 1) / W * b for b in s.bucket_bytes) / step_s / 1e9
 
+    # one launch per bucket (each bucket's ready call separate): step time and
     # per-bucket kernel rates (median over steps)
     import numpy as np
+    for _ in range(5):
+        s.step(per_bucket=True)
+    pb_elapsed = s.timed(args.steps, per_bucket=True) / args.steps
+    ddp.ddp_set_timing(s.r, True)
+    s.timed(args.steps, per_bucket=True)
+    pf, pc, pms = ddp.ddp_get_timings(s.r)
+    ddp.ddp_set_timing(s.r, False)
     per_bucket = {}
     for b in range(s.plan.n_buckets):
-        sel = ms[buckets == b]
+        sel = pms[(pf == b) & (pc == 1)]
         if sel.size:
-            per_elem = 10 if wl.input_mode == 2 else 8
-            nb = per_elem * W * s.bucket_bytes[b] // 4
-            per_bucket[b] = round(nb / (float(np.median(sel)) / 1e3) / 1e9, 1)
+            per_bucket[b] = round(bucket_alg[b] / (float(np.median(sel)) / 1e3) / 1e9, 1)
+    per_bucket_launch = {"ms_per_step": round(pb_elapsed * 1e3, 4),
+                         "GBps": round(bytes_per_step / pb_elapsed / 1e9, 2),
+                         "kernel_GBps_per_bucket": per_bucket if len(per_bucket) <= 16 else None,
+                         "kernel_GBps_all": round(sum(bucket_alg) * args.steps / (float(pms.sum()) / 1e3) / 1e9, 1)
+                         if pms.size else None}
 
     overlap = None
     if args.backward_ms > 0:
@@ -332,9 +352,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "bucket_reduce (reduce_fixed)", "launches": launches,
+                     "buckets_per_launch": round(float(count.mean()), 2) if launches else None,
                      "algorithmic_bytes_per_launch": int(per_launch_bytes),
-                     "avg_launch_us": round(kernel_s / max(launches, 1) * 1e6, 2),
-                     "per_bucket_GBps": per_bucket},
+                     "avg_launch_us": round(kernel_s / max(launches, 1) * 1e6, 2)},
+    "per_bucket_launch": per_bucket_launch,
         "overlap": overlap,
         "cpu_baseline": cpu,
     }

@@ -106,7 +106,7 @@ def lib():
             "ddp_get_ready_order": [P, P, P],
             "ddp_get_launched": [P, P],
             "ddp_set_timing": [P, I32],
-            "ddp_get_timings": [P, P, P, I32, P],
+            "ddp_get_timings": [P, P, P, P, I32, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -299,13 +299,15 @@ def ddp_set_timing(r: Reducer, enable: bool) -> None:
 
 
 def ddp_get_timings(r: Reducer):
-    """(bucket indices, kernel ms) of every launch since timing was enabled."""
+    """(first bucket, buckets covered, kernel ms) of every launch since timing
+    was enabled, as three arrays."""
     n = ctypes.c_int32()
-    _check(lib().ddp_get_timings(r.handle, None, None, 0, ctypes.byref(n)))
-    b = np.empty(max(n.value, 1), np.int32)
-    ms = np.empty(max(n.value, 1), np.float32)
-    _check(lib().ddp_get_timings(r.handle, b.ctypes.data, ms.ctypes.data, n.value, ctypes.byref(n)))
-    return b[:n.value].copy(), ms[:n.value].copy()
+    _check(lib().ddp_get_timings(r.handle, None, None, None, 0, ctypes.byref(n)))
+    m = max(n.value, 1)
+    b, c, ms = np.empty(m, np.int32), np.empty(m, np.int32), np.empty(m, np.float32)
+    _check(lib().ddp_get_timings(r.handle, b.ctypes.data, c.ctypes.data, ms.ctypes.data, n.value, ctypes.byref(n)))
+    k = n.value
+    return b[:k].copy(), c[:k].copy(), ms[:k].copy()
 
 
 def make_reducer(world: int, param_numel: Sequence[int], plan: BucketPlan, input_mode: int,

@@ -207,7 +207,8 @@ struct ddp_reducer {
     hipEvent_t ev_ready = nullptr, ev_done = nullptr;
     bool timing = false;
     std::vector<hipEvent_t> t0, t1;       // event pool, reused across record lists
-    std::vector<int32_t> timed_bucket;    // bucket of each recorded launch
+    std::vector<int32_t> timed_bucket;    // first bucket of each recorded launch
+    std::vector<int32_t> timed_count;     // buckets covered by each recorded launch
     ddp_comm_hook_fn hook = nullptr;
     void *hook_ctx = nullptr;
     // per-iteration state [DDP-ch17 §17.12, §17.16]
@@ -240,7 +241,9 @@ struct ddp_reducer {
 
 namespace {
 
-int enqueue_reduce(ddp_reducer *r, int32_t b, hipStream_t s)
+// Reduction of buckets [b0, b1) (consecutive, so their tiles are one
+// contiguous range of the tile table) as one kernel launch on stream s.
+int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
 {
     if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device buffers");
     hipError_t e;
@@ -248,8 +251,8 @@ int enqueue_reduce(ddp_reducer *r, int32_t b, hipStream_t s)
     if (r->timing) {
         while (r->t0.size() <= slot) {
             hipEvent_t a = nullptr, c = nullptr;
-            e = hipEventCreate(&a);
-            if (e == hipSuccess) e = hipEventCreate(&c);
+            e = hipEventCreateWithFlags(&a, hipEventDisableSystemFence);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&c, hipEventDisableSystemFence);
             if (e != hipSuccess) {
                 if (a) (void)hipEventDestroy(a);
                 return hip_fail("hipEventCreate", e);
@@ -259,25 +262,28 @@ int enqueue_reduce(ddp_reducer *r, int32_t b, hipStream_t s)
         }
         if ((e = hipEventRecord(r->t0[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
     }
-    e = ddp::launch_bucket_reduce(r->pv.mode, r->pv.W, r->scale, r->tables, r->pv.tile_begin[b],
-                                  r->pv.tile_count[b], s);
+    const int32_t tile0 = r->pv.tile_begin[b0];
+    const int32_t tiles = r->pv.tile_begin[b1 - 1] + r->pv.tile_count[b1 - 1] - tile0;
+    e = ddp::launch_bucket_reduce(r->pv.mode, r->pv.W, r->scale, r->tables, tile0, tiles, s);
     if (e != hipSuccess) return hip_fail("bucket reduce launch", e);
     if (r->timing) {
         if ((e = hipEventRecord(r->t1[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
-        r->timed_bucket.push_back(b);
+        r->timed_bucket.push_back(b0);
+        r->timed_count.push_back(b1 - b0);
     }
     return DDP_OK;
 }
 
-// All-reduce of one bucket as issued by the reducer: the comm stream first
-// waits for everything queued on the compute stream (the bucket's gradients
-// were produced there), then the hook or the default reduction runs on it
+// All-reduce of buckets [b0, b1) as issued by the reducer: the comm stream
+// first waits for everything queued on the compute stream (the buckets'
+// gradients were produced there), then the hook runs once per bucket, in
+// order, or the default reduction covers the whole range in one launch
 // [PTD-notes §2.3; MegatronDDP §3]. When the compute stream has already
 // drained, every gradient it produced is complete and visible, so the
-// cross-stream event (a few microseconds of queue latency per bucket) is
-// skipped.
-int launch_bucket(ddp_reducer *r, int32_t b)
+// cross-stream event (a few microseconds of queue latency) is skipped.
+int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
 {
+    if (b0 >= b1) return DDP_OK;
     if (r->device && r->compute != r->comm) {
         hipError_t e = hipStreamQuery(r->compute);
         if (e == hipErrorNotReady) {
@@ -287,13 +293,32 @@ int launch_bucket(ddp_reducer *r, int32_t b)
         if (e != hipSuccess) return hip_fail("stream wait", e);
     }
     if (r->hook) {
-        int rc = r->hook(r->hook_ctx, b);
-        if (rc != 0) return fail(DDP_ERR_HOOK, "communication hook returned " + std::to_string(rc) +
-                                                   " for bucket " + std::to_string(b));
+        for (int32_t b = b0; b < b1; ++b) {
+            int rc = r->hook(r->hook_ctx, b);
+            if (rc != 0) return fail(DDP_ERR_HOOK, "communication hook returned " + std::to_string(rc) +
+                                                       " for bucket " + std::to_string(b));
+        }
         return DDP_OK;
     }
     if (!r->device) return fail(DDP_ERR_INVALID, "no device buffers and no communication hook");
-    return enqueue_reduce(r, b, r->comm);
+    return enqueue_reduce(r, b0, b1, r->comm);
+}
+
+// One gradient-ready mark [DDP-ch17 §17.12]: advances r->next past every
+// bucket that is now launchable, in index order [L15 §2.3]; the caller
+// launches [old next, new next).
+int mark_one(ddp_reducer *r, int32_t param)
+{
+    if (param < 0 || param >= r->pv.P) return fail(DDP_ERR_INVALID, "gradient index out of range");
+    if (r->ready[param])
+        return fail(DDP_ERR_ALREADY_READY,
+                    "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
+    r->ready[param] = 1;
+    r->ready_order.push_back(param);
+    ++r->marks;
+    --r->pending[r->pv.bucket_of[param]];
+    while (r->next < r->pv.B && r->pending[r->next] == 0) ++r->next;
+    return DDP_OK;
 }
 
 void destroy_events(ddp_reducer *r)
@@ -515,21 +540,10 @@ int ddp_prepare_for_backward(ddp_reducer *r)
 int ddp_mark_ready(ddp_reducer *r, int32_t param)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
-    if (param < 0 || param >= r->pv.P) return fail(DDP_ERR_INVALID, "gradient index out of range");
-    if (r->ready[param])
-        return fail(DDP_ERR_ALREADY_READY,
-                    "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
-    r->ready[param] = 1;
-    r->ready_order.push_back(param);
-    ++r->marks;
-    --r->pending[r->pv.bucket_of[param]];
-    // launch strictly by bucket index [DDP-ch17 §17.12; L15 §2.3]
-    while (r->next < r->pv.B && r->pending[r->next] == 0) {
-        const int32_t b = r->next++;
-        int rc = launch_bucket(r, b);
-        if (rc != DDP_OK) return rc;
-    }
-    return DDP_OK;
+    const int32_t b0 = r->next;
+    int rc = mark_one(r, param);
+    if (rc != DDP_OK) return rc;
+    return launch_buckets(r, b0, r->next);
 }
 
 int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done)
@@ -537,12 +551,21 @@ int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_
     if (n_done) *n_done = 0;
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (n < 0 || (n > 0 && !params)) return fail(DDP_ERR_INVALID, "bad parameter list");
-    for (int32_t i = 0; i < n; ++i) {
-        int rc = ddp_mark_ready(r, params[i]);
-        if (rc != DDP_OK) return rc;
-        if (n_done) *n_done = i + 1;
+    const int32_t b0 = r->next;
+    int rc = DDP_OK;
+    for (int32_t i = 0; i < n && rc == DDP_OK; ++i) {
+        rc = mark_one(r, params[i]);
+        if (rc == DDP_OK && n_done) *n_done = i + 1;
     }
-    return DDP_OK;
+    // buckets completed by the marks that succeeded are launched even when a
+    // later mark failed; the first error is the one reported
+    const std::string err = rc != DDP_OK ? g_err : std::string();
+    const int lrc = launch_buckets(r, b0, r->next);
+    if (rc != DDP_OK) {
+        g_err = err;
+        return rc;
+    }
+    return lrc;
 }
 
 int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream)
@@ -551,7 +574,7 @@ int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream)
     if (bucket < 0 || bucket >= r->pv.B) return fail(DDP_ERR_INVALID, "bucket index out of range");
     if (r->in_iteration() && bucket >= r->next)
         return fail(DDP_ERR_ORDER, "bucket " + std::to_string(bucket) + " still waits for gradients");
-    return enqueue_reduce(r, bucket, static_cast<hipStream_t>(stream));
+    return enqueue_reduce(r, bucket, bucket + 1, static_cast<hipStream_t>(stream));
 }
 
 int ddp_finish(ddp_reducer *r, int32_t host_blocking)
@@ -617,17 +640,22 @@ int ddp_set_timing(ddp_reducer *r, int32_t enable)
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device");
     r->timing = enable != 0;
-    if (r->timing) r->timed_bucket.clear();
+    if (r->timing) {
+        r->timed_bucket.clear();
+        r->timed_count.clear();
+    }
     return DDP_OK;
 }
 
-int ddp_get_timings(const ddp_reducer *r, int32_t *buckets, float *ms, int32_t capacity, int32_t *n)
+int ddp_get_timings(const ddp_reducer *r, int32_t *first_bucket, int32_t *n_buckets, float *ms, int32_t capacity,
+                    int32_t *n)
 {
     if (!r || !n || capacity < 0) return fail(DDP_ERR_INVALID, "bad argument");
     *n = int32_t(r->timed_bucket.size());
     const int32_t m = std::min(capacity, *n);
     for (int32_t i = 0; i < m; ++i) {
-        if (buckets) buckets[i] = r->timed_bucket[i];
+        if (first_bucket) first_bucket[i] = r->timed_bucket[i];
+        if (n_buckets) n_buckets[i] = r->timed_count[i];
         if (ms) {
             hipError_t e = hipEventElapsedTime(&ms[i], r->t0[i], r->t1[i]);
             if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);

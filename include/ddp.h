@@ -163,8 +163,13 @@ int ddp_mark_ready(ddp_reducer *r, int32_t param);
 
 /* ddp_mark_ready for params[0], params[1], ... in that order, in one call
  * (gradients that become ready together, e.g. the weight and bias of one
- * layer). Stops at the first error and returns it; *n_done (may be NULL)
- * receives how many marks succeeded. */
+ * layer, or every gradient at once after a backward without overlap).
+ * Buckets completed by the call are launched at its end, in index order;
+ * without a registered hook, consecutive ones go out as ONE kernel launch (a
+ * coalesced bucket group [MegatronDDP §3]), results identical to separate
+ * launches. Stops at the first failing mark and returns its error (buckets
+ * completed before it are still launched); *n_done (may be NULL) receives how
+ * many marks succeeded. */
 int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done);
 
 /* The default communication hook: enqueues the reduction of `bucket` on
@@ -205,15 +210,18 @@ int ddp_get_ready_order(const ddp_reducer *r, int32_t *order, int32_t *n);
 /* Buckets launched since the last reset. */
 int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched);
 
-/* Per-launch timing: while enabled, each default bucket reduction is
- * bracketed by two HIP events on the stream it runs on. Enabling (again)
- * starts a new record list; the events are kept and reused.
+/* Per-launch timing: while enabled, each default reduction launch (one
+ * bucket, or a coalesced group) is bracketed by two HIP events on the stream
+ * it runs on (timing-only events, without the system-scope fence). Enabling
+ * (again) starts a new record list; the events are kept and reused.
  * ddp_get_timings copies up to `capacity` records (launch order) of the
- * launches since timing was last enabled: the bucket index and the kernel's
- * duration in ms. The caller must first wait for those launches to complete
- * (e.g. ddp_finish with host_blocking). *n = number of records. */
+ * launches since timing was last enabled: the first bucket, the number of
+ * buckets the launch covered, and the kernel's duration in ms. The caller
+ * must first wait for those launches to complete (e.g. ddp_finish with
+ * host_blocking). *n = number of records. Any output array may be NULL. */
 int ddp_set_timing(ddp_reducer *r, int32_t enable);
-int ddp_get_timings(const ddp_reducer *r, int32_t *buckets, float *ms, int32_t capacity, int32_t *n);
+int ddp_get_timings(const ddp_reducer *r, int32_t *first_bucket, int32_t *n_buckets, float *ms, int32_t capacity,
+                    int32_t *n);
 
 /* Text of the last error on this thread ("" if none). Never NULL. */
 const char *ddp_last_error(void);

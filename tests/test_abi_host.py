@@ -297,3 +297,20 @@ def test_mark_ready_many_equals_single_marks():
         ddp.ddp_mark_ready_many(r2, [order[0], order[1], order[1], order[2]])
     assert e.value.code == ddp.DDP_ERR_ALREADY_READY and e.value.n_done == 2
     assert ddp.ddp_get_ready_order(r2) == order[:2]
+
+
+def test_mark_ready_many_calls_the_hook_once_per_bucket():
+    """With a registered hook a batch that completes several buckets still
+    calls the hook per bucket, in index order."""
+    r, plan, log = host_reducer([2] * 8, 16, 16)      # 8-byte gradients, 2 per bucket
+    assert plan.n_buckets == 4
+    ddp.ddp_mark_ready_many(r, list(range(7, -1, -1)))
+    assert log == [0, 1, 2, 3]
+
+
+def test_mark_ready_many_launches_completed_buckets_before_reporting_an_error():
+    r, plan, log = host_reducer([2] * 8, 16, 16)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready_many(r, [7, 6, 5, 5])
+    assert e.value.code == ddp.DDP_ERR_ALREADY_READY and e.value.n_done == 3
+    assert log == [0]

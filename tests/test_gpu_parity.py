@@ -238,9 +238,36 @@ def test_timing_records_every_launch():
     run.ddp.ddp_set_timing(run.r, True)
     for _ in range(3):
         run.step()
-    b, ms = run.ddp.ddp_get_timings(run.r)
-    assert list(b) == [0, 1, 2] * 3
+    b, c, ms = run.ddp.ddp_get_timings(run.r)
+    assert list(b) == [0, 1, 2] * 3 and list(c) == [1] * 9
     assert np.all(ms > 0) and np.all(ms < 100)
+    run.close()
+
+
+def test_batched_marks_coalesce_ready_buckets_into_one_launch():
+    """All gradients marked in one call: the three buckets go out as one
+    launch, with results identical to separate launches."""
+    from synth import workloads as wls
+    wl = wls.tiny()
+    run = Run(wl)
+    ddp = run.ddp
+    ddp.ddp_set_timing(run.r, True)
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_mark_ready_many(run.r, list(range(len(wl.numel) - 1, -1, -1)))
+    ddp.ddp_finish(run.r, host_blocking=True)
+    b, c, ms = ddp.ddp_get_timings(run.r)
+    assert list(b) == [0] and list(c) == [3]
+    check_full(run)
+    # two calls: bucket 0 alone, then buckets 1 and 2 together
+    run.inputs.refill()
+    ddp.ddp_set_timing(run.r, True)
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_mark_ready_many(run.r, [7, 6, 5, 4])
+    ddp.ddp_mark_ready_many(run.r, [3, 2, 1, 0])
+    ddp.ddp_finish(run.r, host_blocking=True)
+    b, c, ms = ddp.ddp_get_timings(run.r)
+    assert list(b) == [0, 1] and list(c) == [1, 2]
+    check_full(run)
     run.close()
 
 
