@@ -86,15 +86,27 @@ class Session:
         self.compute = torch.cuda.Stream()
         self.comm = torch.cuda.Stream()
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
-                                  self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream)
+                                  self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
+                                  collective=wl.collective)
         self.order = np.arange(len(wl.numel) - 1, -1, -1, dtype=np.int32)
         self.members = [np.asarray(m, np.int32) for m in self.plan.buckets()]
 
-    def step(self, backward_us: float = 0.0, serial: bool = False, per_bucket: bool = False):
+    def step(self, backward_us: float = 0.0, serial: bool = False, per_bucket: bool = False,
+             backward_only: bool = False):
         """per_bucket: one ready call per bucket, so each bucket is its own
         launch; otherwise all gradients are marked in one call and the
-        buckets go out as one coalesced launch."""
+        buckets go out as one coalesced launch. backward_us > 0: a synthetic
+        backward on the compute stream, one piece per bucket in proportion to
+        its bytes, each followed by that bucket's ready call (serial: the
+        whole backward first, then the ready calls); backward_only: the
+        pieces alone, no reduction."""
         ddp = self.ddp
+        if backward_only:
+            import synth
+            tot = float(sum(self.bucket_bytes)) or 1.0
+            for b in range(len(self.members)):
+                synth.spin_dev(backward_us * self.bucket_bytes[b] / tot, self.compute.cuda_stream)
+            return
         ddp.ddp_prepare_for_backward(self.r)
         if backward_us <= 0 and not per_bucket:
             ddp.ddp_mark_ready_many(self.r, self.order)
@@ -105,13 +117,25 @@ class Session:
             import synth
             tot = float(sum(self.bucket_bytes)) or 1.0
             cs = self.compute.cuda_stream
-            if serial:
-                synth.spin_dev(backward_us, cs)
             for b, members in enumerate(self.members):
                 if not serial:
                     synth.spin_dev(backward_us * self.bucket_bytes[b] / tot, cs)
-                ddp.ddp_mark_ready_many(self.r, members)
+                elif b == 0:
+                    for bb in range(len(self.members)):
+                        synth.spin_dev(backward_us * self.bucket_bytes[bb] / tot, cs)
+                if not serial:
+                    ddp.ddp_mark_ready_many(self.r, members)
+            if serial:
+                for members in self.members:
+                    ddp.ddp_mark_ready_many(self.r, members)
         ddp.ddp_finish(self.r, host_blocking=False)
+
+    def close(self):
+        self.ddp.ddp_reducer_destroy(self.r)
+        self.r = None
+        del self.inputs
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
 
     def timed(self, steps: int, **kw):
         torch = self.torch
@@ -191,7 +215,7 @@ def cpu_baseline(wl, session, target_s: float):
     gbps_1 = acc / t1 / 1e9
     gbps_mt = acc * reps_mt / tmt / 1e9
     match = None
-    if session is not None:
+    if session is not None and wl.collective == 0:
         match = True
         for b, out in zip(chosen, outs):
             lo = sum(oplan.bucket_bytes[:b]) // 4
@@ -209,6 +233,53 @@ def cpu_baseline(wl, session, target_s: float):
     }
 
 
+def run_sweep(args):
+    """Bucket-size sweep (60M fp32 parameters as 6000 tensors of 10K): for
+    every W and cap, the reduction alone (one launch per bucket and
+    coalesced), and the step with a synthetic backward overlapped and in
+    series."""
+    from synth import workloads as wls
+    rows = []
+    worlds = [int(x) for x in args.sweep_worlds.split(",")]
+    caps = [int(x) for x in args.sweep_caps.split(",")]
+    for W in worlds:
+        for cap in caps:
+            wl = wls.sweep(W, cap)
+            s = Session(wl)
+            nbytes = wl.algorithmic_bytes()
+            # size the timed region to about 50 ms
+            t1 = s.timed(1, per_bucket=True)
+            k = max(3, min(200, int(0.05 / max(t1, 1e-6))))
+            s.timed(2, per_bucket=True)
+            t_pb = s.timed(k, per_bucket=True) / k
+            s.timed(2)
+            t_co = s.timed(k) / k
+            us = args.backward_ms * 1e3
+            s.timed(1, backward_us=us, backward_only=True)
+            t_bw = s.timed(args.overlap_steps, backward_us=us, backward_only=True) / args.overlap_steps
+            s.timed(1, backward_us=us)
+            t_ov = s.timed(args.overlap_steps, backward_us=us) / args.overlap_steps
+            t_se = s.timed(args.overlap_steps, backward_us=us, serial=True) / args.overlap_steps
+            row = {"world": W, "cap_mib": cap, "buckets": s.plan.n_buckets,
+                   "bytes_per_step": nbytes,
+                   "per_bucket_launch_ms": round(t_pb * 1e3, 4), "per_bucket_launch_GBps": round(nbytes / t_pb / 1e9, 1),
+                   "coalesced_ms": round(t_co * 1e3, 4), "coalesced_GBps": round(nbytes / t_co / 1e9, 1),
+                   "backward_alone_ms": round(t_bw * 1e3, 3),
+                   "overlapped_step_ms": round(t_ov * 1e3, 3),
+                   "serial_step_ms": round(t_se * 1e3, 3),
+                   "exposed_ms": round((t_ov - t_bw) * 1e3, 3)}
+            log(json.dumps(row))
+            rows.append(row)
+            s.close()
+    out = {"sweep": "60M fp32 params as 6000 tensors of 10K, U(-1,1); first bucket cap = cap",
+           "backward_ms": args.backward_ms, "rows": rows}
+    text = json.dumps(out)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(text + "\n")
+    print(text, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,11 +287,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="resnet50",
                     help="tiny | resnet50 | bert_large | megatron_llama1b | sweep_w{W}_cap{MiB}")
+    ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-ms", type=float, default=20.0,
                     help="synthetic backward for the overlap measurement (0 disables it)")
     ap.add_argument("--overlap-steps", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true", help="run the bucket-size sweep instead of one workload")
+    ap.add_argument("--sweep-worlds", default="2,4,8,16,32")
+    ap.add_argument("--sweep-caps", default="0,1,5,10,25,50,100,200")
+    ap.add_argument("--sweep-out", default="")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this size (for HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -256,7 +332,14 @@ def main():
         print(json.dumps({"copy_bytes": nbytes, "read_plus_write_GBps": round(2 * nbytes / dt / 1e9, 1)}))
         return
 
+    if args.sweep:
+        run_sweep(args)
+        return
+
     wl = wls.by_name(args.workload)
+    if args.collective == "reduce_scatter":
+        wl.collective = wls.REDUCE_SCATTER
+        wl.name += "_rs"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
     s = Session(wl)
@@ -280,8 +363,9 @@ def main():
     step_s = elapsed / args.steps
     value = bytes_per_step / step_s / 1e9
     W = wl.world
-    per_elem = 10 if wl.input_mode == 2 else 8
-    bucket_alg = [per_elem * W * b // 4 for b in s.bucket_bytes]
+    read = 6 if wl.input_mode == 2 else 4
+    per_elem = read * W + 4 if wl.collective == wls.REDUCE_SCATTER else (read + 4) * W
+    bucket_alg = [per_elem * b // 4 for b in s.bucket_bytes]
     launch_bytes = [sum(bucket_alg[f:f + c]) for f, c in zip(first, count)]
     kernel_s = float(ms.sum()) / 1e3
     launches = len(ms)
@@ -346,6 +430,7 @@ def main():
         "config": {"workload": wl.name, "world": W, "tensors": len(wl.numel), "elements": wl.total_numel,
                    "buckets": s.plan.n_buckets, "cap_bytes": wl.cap_bytes, "first_cap_bytes": wl.first_cap_bytes,
                    "input_mode": MODE_NAMES[wl.input_mode], "bytes_per_step": bytes_per_step,
+                   "collective": "reduce_scatter" if wl.collective == wls.REDUCE_SCATTER else "all_reduce",
                    "parallelism": "1 GPU, W replicas in HBM"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "bus_bw_GBps": round(bus, 2),
@@ -360,7 +445,7 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    ddp.ddp_reducer_destroy(s.r)
+    s.close()
 
 
 if __name__ == "__main__":

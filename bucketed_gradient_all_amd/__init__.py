@@ -33,6 +33,9 @@ DDP_ORDER_REVERSE = 0
 DDP_ORDER_GIVEN = 1
 DDP_ORDER_FWD_THEN_REVERSE = 2
 
+DDP_ALL_REDUCE = 0
+DDP_REDUCE_SCATTER = 1
+
 DDP_IN_F32_COPY = 0
 DDP_IN_F32_VIEW = 1
 DDP_IN_BF16_ACCUM_F32 = 2
@@ -77,6 +80,7 @@ class ddp_reducer_desc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("compute_stream", ctypes.c_void_p),
         ("comm_stream", ctypes.c_void_p),
+        ("collective", ctypes.c_int32),
     ]
 
 
@@ -171,7 +175,8 @@ class Desc:
     def __init__(self, world: int, param_numel: Sequence[int], bucket_of: Sequence[int],
                  offset_in_bucket: Sequence[int], n_buckets: int, input_mode: int = DDP_IN_F32_COPY,
                  grads: Optional[Sequence[Sequence[int]]] = None, flat: Optional[Sequence[int]] = None,
-                 workspace: int = 0, workspace_bytes: int = 0, compute_stream: int = 0, comm_stream: int = 0):
+                 workspace: int = 0, workspace_bytes: int = 0, compute_stream: int = 0, comm_stream: int = 0,
+                 collective: int = DDP_ALL_REDUCE):
         self.numel = np.ascontiguousarray(param_numel, dtype=np.int64)
         self.bucket_of = np.ascontiguousarray(bucket_of, dtype=np.int32)
         self.offset = np.ascontiguousarray(offset_in_bucket, dtype=np.int64)
@@ -195,6 +200,7 @@ class Desc:
         d.workspace_bytes = workspace_bytes
         d.compute_stream = compute_stream or None
         d.comm_stream = comm_stream or None
+        d.collective = collective
         self.c = d
 
     def set_workspace(self, ptr: int, nbytes: int) -> None:
@@ -312,13 +318,14 @@ def ddp_get_timings(r: Reducer):
 
 def make_reducer(world: int, param_numel: Sequence[int], plan: BucketPlan, input_mode: int,
                  grad_ptrs: Optional[Sequence[Sequence[int]]], flat_ptrs: Sequence[int],
-                 compute_stream: int, comm_stream: int) -> Reducer:
+                 compute_stream: int, comm_stream: int, collective: int = DDP_ALL_REDUCE) -> Reducer:
     """Creates a device reducer; the workspace is a torch allocation kept
     alive by the returned handle."""
     import torch
 
     desc = Desc(world, param_numel, plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, input_mode,
-                grads=grad_ptrs, flat=flat_ptrs, compute_stream=compute_stream, comm_stream=comm_stream)
+                grads=grad_ptrs, flat=flat_ptrs, compute_stream=compute_stream, comm_stream=comm_stream,
+                collective=collective)
     nbytes = ddp_workspace_bytes(desc)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     desc.set_workspace(ws.data_ptr(), nbytes)

@@ -24,6 +24,8 @@
 //     data so it does not evict other lines from L2 / MALL;
 //   * fp32 adds and multiplies are issued as separate round-to-nearest
 //     operations (no contraction), so results equal the CPU oracle bit for bit.
+// The reduce-scatter variant (ZeRO-1 [MegatronDDP §3]) folds the same way but
+// stores chunk c only to replica c's flat buffer.
 #include "internal.h"
 
 #include <hip/hip_runtime.h>
@@ -134,7 +136,7 @@ __device__ __forceinline__ const unsigned short *src_bf16(const KernelTables &T,
 // One element, any W: used for unaligned heads and tails and for segments
 // whose pointers do not allow 16-byte vectors.
 template <int MODE>
-__device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t e, float s, int W)
+__device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t e, float s, int W, bool rs)
 {
     float acc = 0.0f;
     for (int k = 0; k < W; ++k) {
@@ -144,34 +146,39 @@ __device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t 
         float t = term1<MODE>(x, g, s);
         acc = k == 0 ? t : __fadd_rn(acc, t);
     }
+    if (rs) {
+        st1(T.flat[sg.chunk] + sg.flat + e, acc);
+        return;
+    }
     for (int w = 0; w < W; ++w) st1(T.flat[w] + sg.flat + e, acc);
 }
 
 // Heads, tails and scalar-only segments of a tile.
 template <int MODE>
 __device__ __forceinline__ void scalar_parts(const KernelTables &T, const DeviceSeg &sg, int64_t tin, int64_t tile,
-                                             float s, int W)
+                                             float s, int W, bool rs)
 {
     const int tid = threadIdx.x;
     if (sg.head >= 0) {
         if (tin != 0) return;
         const int64_t body = (sg.len - sg.head) / 4 * 4;
         const int64_t tail = sg.len - sg.head - body;
-        if (tid < sg.head) fold_scalar<MODE>(T, sg, tid, s, W);
-        if (tid >= 64 && tid < 64 + tail) fold_scalar<MODE>(T, sg, sg.head + body + (tid - 64), s, W);
+        if (tid < sg.head) fold_scalar<MODE>(T, sg, tid, s, W, rs);
+        if (tid >= 64 && tid < 64 + tail) fold_scalar<MODE>(T, sg, sg.head + body + (tid - 64), s, W, rs);
         return;
     }
     const int64_t base = tin * tile;
     for (int64_t j = tid; j < tile; j += kThreads) {
         const int64_t e = base + j;
-        if (e < sg.len) fold_scalar<MODE>(T, sg, e, s, W);
+        if (e < sg.len) fold_scalar<MODE>(T, sg, e, s, W, rs);
     }
 }
 
-// One element with W known at compile time, from hoisted pointers.
-template <int W, int MODE>
+// One element with W known at compile time, from hoisted pointers; the sum
+// goes to the NOUT destinations (all W replicas, or the chunk's owner).
+template <int W, int NOUT, int MODE>
 __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
-                                                  float *const (&ds)[W], int64_t e, float s)
+                                                  float *const (&ds)[NOUT], int64_t e, float s)
 {
     float t[W];
 #pragma unroll
@@ -180,7 +187,7 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 #pragma unroll
     for (int k = 1; k < W; ++k) acc = __fadd_rn(acc, t[k]);
 #pragma unroll
-    for (int w = 0; w < W; ++w) st1(ds[w] + e, acc);
+    for (int w = 0; w < NOUT; ++w) st1(ds[w] + e, acc);
 }
 
 // The 16-byte-vector part of one tile: U groups of 4 elements per thread.
@@ -189,9 +196,9 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // then all stores. CHECK = true: the segment's last tile, with per-lane
 // bounds; out-of-range lanes load the segment's first vector (in bounds, value
 // unused) and skip their stores.
-template <int W, int MODE, bool CHECK>
+template <int W, int NOUT, int MODE, bool CHECK>
 __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
-                                            float *const (&ds)[W], const DeviceSeg &sg, int64_t tin, float s)
+                                            float *const (&ds)[NOUT], const DeviceSeg &sg, int64_t tin, float s)
 {
     constexpr int U = unroll_for(W);
     constexpr int64_t TILE = tile_elems(W);
@@ -224,7 +231,7 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
     for (int u = 0; u < U; ++u)
         if (ok[u]) {
 #pragma unroll
-            for (int w = 0; w < W; ++w) st4(ds[w] + e[u], acc[u]);
+            for (int w = 0; w < NOUT; ++w) st4(ds[w] + e[u], acc[u]);
         }
 }
 
@@ -233,9 +240,10 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
 // the first store, so they stay in scalar registers; a table read after a
 // store would have to go through the vector memory path and wait for every
 // outstanding store.
-template <int W, int MODE>
+template <int W, int MODE, bool RS>
 __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, float s)
 {
+    constexpr int NOUT = RS ? 1 : W;
     constexpr int64_t TILE = tile_elems(W);
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
@@ -244,39 +252,45 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
     // slot k holds replica (chunk + k) mod W, so the fold is slot 0, 1, ..., W-1
     const float *xs[W];
     const unsigned short *gs[W];
-    float *ds[W];
+    float *ds[NOUT];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         const int r = slot_replica(sg.chunk, k, W);
         xs[k] = src_f32<MODE>(T, sg, r);
         gs[k] = MODE == MODE_BF16 ? src_bf16(T, sg, r) : nullptr;
     }
+    if (RS) {
+        ds[0] = T.flat[sg.chunk] + sg.flat;   // chunk c belongs to replica c
+    } else {
 #pragma unroll
-    for (int w = 0; w < W; ++w) ds[w] = T.flat[w] + sg.flat;
+        for (int w = 0; w < NOUT; ++w) ds[w] = T.flat[w] + sg.flat;
+    }
 
     const int tid = int(threadIdx.x);
     if (sg.head >= 0) {
         if (sg.head + (tin + 1) * TILE <= sg.len)
-            vector_tile<W, MODE, false>(xs, gs, ds, sg, tin, s);
+            vector_tile<W, NOUT, MODE, false>(xs, gs, ds, sg, tin, s);
         else if (sg.len - sg.head >= 4)
-            vector_tile<W, MODE, true>(xs, gs, ds, sg, tin, s);
+            vector_tile<W, NOUT, MODE, true>(xs, gs, ds, sg, tin, s);
         if (tin == 0) {
             const int64_t body = (sg.len - sg.head) / 4 * 4;
             const int64_t tail = sg.len - sg.head - body;
-            if (tid < sg.head) fold_scalar_fixed<W, MODE>(xs, gs, ds, tid, s);
-            if (tid >= 64 && tid < 64 + tail) fold_scalar_fixed<W, MODE>(xs, gs, ds, sg.head + body + (tid - 64), s);
+            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE>(xs, gs, ds, tid, s);
+            if (tid >= 64 && tid < 64 + tail)
+                fold_scalar_fixed<W, NOUT, MODE>(xs, gs, ds, sg.head + body + (tid - 64), s);
         }
         return;
     }
     for (int64_t j = tid; j < TILE; j += kThreads) {
         const int64_t e = tin * TILE + j;
-        if (e < sg.len) fold_scalar_fixed<W, MODE>(xs, gs, ds, e, s);
+        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE>(xs, gs, ds, e, s);
     }
 }
 
 // Any W: replicas are taken eight at a time, in fold order.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32_t tile_begin, float s, int W)
+__global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32_t tile_begin, float s, int W,
+                                                           int rs)
 {
     const int64_t TILE = tile_elems(W);
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
@@ -307,49 +321,58 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
                     }
                 }
             }
-            for (int w = 0; w < W; ++w) st4(T.flat[w] + sg.flat + e, acc);
+            if (rs) {
+                st4(T.flat[sg.chunk] + sg.flat + e, acc);
+            } else {
+                for (int w = 0; w < W; ++w) st4(T.flat[w] + sg.flat + e, acc);
+            }
         }
     }
-    scalar_parts<MODE>(T, sg, tin, TILE, s, W);
+    scalar_parts<MODE>(T, sg, tin, TILE, s, W, rs != 0);
 }
 
 template <int W, int MODE>
-hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, float s, hipStream_t st)
+hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, float s, bool rs, hipStream_t st)
 {
-    hipLaunchKernelGGL((reduce_fixed<W, MODE>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s);
+    if (rs)
+        hipLaunchKernelGGL((reduce_fixed<W, MODE, true>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s);
+    else
+        hipLaunchKernelGGL((reduce_fixed<W, MODE, false>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s);
     return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch(int W, const KernelTables &t, int32_t tile_begin, int32_t n_tiles, float s, hipStream_t st)
+hipError_t dispatch(int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles, float s,
+                    hipStream_t st)
 {
     switch (W) {
-    case 1: return launch_fixed<1, MODE>(t, tile_begin, n_tiles, s, st);
-    case 2: return launch_fixed<2, MODE>(t, tile_begin, n_tiles, s, st);
-    case 3: return launch_fixed<3, MODE>(t, tile_begin, n_tiles, s, st);
-    case 4: return launch_fixed<4, MODE>(t, tile_begin, n_tiles, s, st);
-    case 5: return launch_fixed<5, MODE>(t, tile_begin, n_tiles, s, st);
-    case 6: return launch_fixed<6, MODE>(t, tile_begin, n_tiles, s, st);
-    case 7: return launch_fixed<7, MODE>(t, tile_begin, n_tiles, s, st);
-    case 8: return launch_fixed<8, MODE>(t, tile_begin, n_tiles, s, st);
-    case 16: return launch_fixed<16, MODE>(t, tile_begin, n_tiles, s, st);
-    case 32: return launch_fixed<32, MODE>(t, tile_begin, n_tiles, s, st);
+    case 1: return launch_fixed<1, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 2: return launch_fixed<2, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 3: return launch_fixed<3, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 4: return launch_fixed<4, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 5: return launch_fixed<5, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 6: return launch_fixed<6, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 7: return launch_fixed<7, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 8: return launch_fixed<8, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 16: return launch_fixed<16, MODE>(t, tile_begin, n_tiles, s, rs, st);
+    case 32: return launch_fixed<32, MODE>(t, tile_begin, n_tiles, s, rs, st);
     default:
-        hipLaunchKernelGGL((reduce_generic<MODE>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s, W);
+        hipLaunchKernelGGL((reduce_generic<MODE>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s, W,
+                           rs ? 1 : 0);
         return hipGetLastError();
     }
 }
 
 }  // namespace
 
-hipError_t launch_bucket_reduce(int mode, int W, float scale, const KernelTables &t, int32_t tile_begin,
-                                int32_t n_tiles, hipStream_t s)
+hipError_t launch_bucket_reduce(int mode, int W, bool reduce_scatter, float scale, const KernelTables &t,
+                                int32_t tile_begin, int32_t n_tiles, hipStream_t s)
 {
     if (n_tiles <= 0) return hipSuccess;
     switch (mode) {
-    case MODE_COPY: return dispatch<MODE_COPY>(W, t, tile_begin, n_tiles, scale, s);
-    case MODE_VIEW: return dispatch<MODE_VIEW>(W, t, tile_begin, n_tiles, scale, s);
-    case MODE_BF16: return dispatch<MODE_BF16>(W, t, tile_begin, n_tiles, scale, s);
+    case MODE_COPY: return dispatch<MODE_COPY>(W, reduce_scatter, t, tile_begin, n_tiles, scale, s);
+    case MODE_VIEW: return dispatch<MODE_VIEW>(W, reduce_scatter, t, tile_begin, n_tiles, scale, s);
+    case MODE_BF16: return dispatch<MODE_BF16>(W, reduce_scatter, t, tile_begin, n_tiles, scale, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -46,9 +46,10 @@ struct KernelTables {
     int32_t n_params;
 };
 
-// Enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on stream s.
-// Returns hipSuccess or the launch error.
-hipError_t launch_bucket_reduce(int mode, int W, float scale, const KernelTables &t, int32_t tile_begin,
-                                int32_t n_tiles, hipStream_t s);
+// Enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on stream s:
+// all-reduce (the sum stored to every replica) or reduce-scatter (chunk c
+// stored to replica c only). Returns hipSuccess or the launch error.
+hipError_t launch_bucket_reduce(int mode, int W, bool reduce_scatter, float scale, const KernelTables &t,
+                                int32_t tile_begin, int32_t n_tiles, hipStream_t s);
 
 }  // namespace ddp

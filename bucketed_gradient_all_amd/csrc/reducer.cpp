@@ -59,6 +59,7 @@ size_t align_up(size_t x)
 // Plan data validated and normalised from a desc.
 struct PlanView {
     int32_t W = 0, P = 0, B = 0, mode = 0;
+    bool reduce_scatter = false;
     std::vector<int64_t> numel;
     std::vector<int32_t> bucket_of;
     std::vector<int64_t> offset;                 // bytes inside the bucket
@@ -134,12 +135,15 @@ int validate(const ddp_reducer_desc *d, PlanView &pv)
     if (d->n_params < 0 || d->n_buckets < 0) return fail(DDP_ERR_INVALID, "negative parameter or bucket count");
     if (d->input_mode < DDP_IN_F32_COPY || d->input_mode > DDP_IN_BF16_ACCUM_F32)
         return fail(DDP_ERR_INVALID, "unknown input mode");
+    if (d->collective != DDP_ALL_REDUCE && d->collective != DDP_REDUCE_SCATTER)
+        return fail(DDP_ERR_INVALID, "unknown collective");
     if (d->n_params > 0 && (!d->param_numel || !d->bucket_of || !d->offset_in_bucket))
         return fail(DDP_ERR_INVALID, "plan arrays are NULL");
     pv.W = d->world;
     pv.P = d->n_params;
     pv.B = d->n_buckets;
     pv.mode = d->input_mode;
+    pv.reduce_scatter = d->collective == DDP_REDUCE_SCATTER;
     pv.numel.assign(d->param_numel, d->param_numel + pv.P);
     pv.bucket_of.assign(d->bucket_of, d->bucket_of + pv.P);
     pv.offset.assign(d->offset_in_bucket, d->offset_in_bucket + pv.P);
@@ -264,7 +268,7 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
     }
     const int32_t tile0 = r->pv.tile_begin[b0];
     const int32_t tiles = r->pv.tile_begin[b1 - 1] + r->pv.tile_count[b1 - 1] - tile0;
-    e = ddp::launch_bucket_reduce(r->pv.mode, r->pv.W, r->scale, r->tables, tile0, tiles, s);
+    e = ddp::launch_bucket_reduce(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
     if (e != hipSuccess) return hip_fail("bucket reduce launch", e);
     if (r->timing) {
         if ((e = hipEventRecord(r->t1[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);

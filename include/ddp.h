@@ -105,6 +105,15 @@ int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t
 /* ---------------------------------------------------------------------------
  * Reducer: one model's gradients over W replicas, reduced bucket by bucket.
  * ------------------------------------------------------------------------- */
+enum {
+    DDP_ALL_REDUCE = 0,      /* every replica receives the whole reduced bucket (DDP) [DDP-ch17 §17.4]     */
+    DDP_REDUCE_SCATTER = 1   /* replica c receives only ring chunk c of it (ZeRO-1, distributed optimizer)
+                                [MegatronDDP §3]; chunk c = [c*q, min((c+1)*q, n)), q = ceil(n/W). The
+                                sum is folded exactly as for DDP_ALL_REDUCE, so the owned shard is bit-identical
+                                to the same slice of the all-reduce result; the rest of each replica's flat
+                                buffer is left as it was (in-place modes: unreduced input).             */
+};
+
 typedef struct ddp_reducer ddp_reducer;   /* opaque, owned by the library */
 
 typedef struct {
@@ -130,6 +139,7 @@ typedef struct {
     void *compute_stream;              /* hipStream_t on which gradients are produced               */
     void *comm_stream;                 /* hipStream_t on which bucket reductions run (a side
                                           stream that overlaps backward [PTD-notes §2.3])           */
+    int32_t collective;                /* DDP_ALL_REDUCE (0) or DDP_REDUCE_SCATTER                  */
 } ddp_reducer_desc;
 
 /* Device workspace the reducer needs for its tables (segments, tiles,
@@ -184,7 +194,8 @@ int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_
  * acc = t_c, then acc += t_{c+1}, ..., t_{c+W-1} (indices mod W), each an
  * fp32 add rounded to nearest even: the value the ring reduce-scatter leaves
  * for chunk c [DDP-ch17 §17.4, §17.9; MegatronDDP §3]. acc is written to
- * element e of all W flat buffers (the all-gather). */
+ * element e of all W flat buffers (the all-gather), or, for
+ * DDP_REDUCE_SCATTER, to replica c's flat buffer only. */
 int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
 
 /* End of backward [DDP-ch17 §17.41; MegatronDDP §5]: checks that every bucket

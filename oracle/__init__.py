@@ -21,13 +21,14 @@ Parts:
   fold.c / fold.py O3  mean over W replicas in the ring all-reduce's fold order (fp32, C)
                    O5  the same fold split over host threads (identical bits)
   ring.py          O4  literal ring reduce-scatter + all-gather simulation (tiny inputs)
+  fold.py          O6  reduce-scatter only (ZeRO-1): replica c keeps chunk c of the mean
 
 Every function is pinned by tests under ``tests/`` (``-m "not gpu"``) against
 the pages' worked examples, closed forms, brute force and invariants.
 """
 from .plan import Plan, plan_buckets, REVERSE, GIVEN, FWD_THEN_REVERSE  # noqa: F401
 from .reducer_model import ReducerModel, ModelError, comm_timeline  # noqa: F401
-from .ring import ring_allreduce  # noqa: F401
+from .ring import ring_allreduce, ring_reduce_scatter  # noqa: F401
 from . import fold  # noqa: F401
 
 

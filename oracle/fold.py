@@ -1,4 +1,5 @@
-"""ctypes front of oracle/fold.c (O3, O5). TEST INFRASTRUCTURE ONLY."""
+"""ctypes front of oracle/fold.c (O3, O5) and the reduce-scatter result (O6).
+TEST INFRASTRUCTURE ONLY."""
 from __future__ import annotations
 
 import ctypes
@@ -113,3 +114,24 @@ def reduce_at_bf16acc(n: int, elems: np.ndarray, main_vals: np.ndarray, wg_vals:
     if rc != 0:
         raise ValueError("oracle_reduce_at_bf16acc rejected its arguments")
     return out
+
+
+def chunk_bounds(n: int, W: int):
+    """Ring chunk c = [c*q, min((c+1)*q, n)), q = ceil(n/W)."""
+    q = -(-n // W) if n else 0
+    return [(min(c * q, n), min((c + 1) * q, n)) for c in range(W)]
+
+
+def reduce_scatter_f32(x: Sequence[np.ndarray]):
+    """Reduce-scatter of a bucket (ZeRO-1 path [MegatronDDP §3]): replica c
+    receives only chunk c of the mean. Reading: the sum order is the
+    all-reduce's (chunk c folded from replica c on), so the owned shard is
+    bit-identical to the same slice of the all-reduce result.
+    Returns [(lo, hi, values)] per replica."""
+    full = reduce_f32(x)
+    return [(lo, hi, full[lo:hi]) for lo, hi in chunk_bounds(full.size, len(x))]
+
+
+def reduce_scatter_bf16acc(main: Sequence[np.ndarray], wgrad: Sequence[np.ndarray]):
+    full = reduce_bf16acc(main, wgrad)
+    return [(lo, hi, full[lo:hi]) for lo, hi in chunk_bounds(full.size, len(main))]

@@ -67,3 +67,28 @@ def ring_allreduce(grads: Sequence[np.ndarray], wgrad_bf16: Optional[Sequence[np
         for dst, lo, hi, data in sends:
             bufs[dst][lo:hi] = data
     return bufs
+
+
+def ring_reduce_scatter(grads: Sequence[np.ndarray]) -> List[tuple]:
+    """Reduce-scatter phase only, step by step as in ring_allreduce. After it,
+    rank r holds the fully reduced chunk (r + 1) mod W. Returns, per chunk c,
+    (rank holding it, lo, hi, values)."""
+    W = len(grads)
+    n = grads[0].size
+    s = np.float32(1.0) / np.float32(W)
+    bufs = [(np.array(g, dtype=np.float32) * s).astype(np.float32) for g in grads]
+    ch = _chunks(n, W)
+    for step in range(W - 1):
+        sends = []
+        for r in range(W):
+            c = (r - step) % W
+            lo, hi = ch[c]
+            sends.append(((r + 1) % W, lo, hi, bufs[r][lo:hi].copy()))
+        for dst, lo, hi, data in sends:
+            bufs[dst][lo:hi] = (bufs[dst][lo:hi] + data).astype(np.float32)
+    out = []
+    for c in range(W):
+        holder = (c - 1) % W
+        lo, hi = ch[c]
+        out.append((holder, lo, hi, bufs[holder][lo:hi].copy()))
+    return out

@@ -36,6 +36,10 @@ IN_F32_COPY = 0
 IN_F32_VIEW = 1
 IN_BF16_ACCUM_F32 = 2
 
+# collectives (same numbering as include/ddp.h)
+ALL_REDUCE = 0
+REDUCE_SCATTER = 1
+
 # order modes (same numbering as include/ddp.h)
 ORDER_REVERSE = 0
 ORDER_GIVEN = 1
@@ -54,6 +58,7 @@ class Workload:
     input_mode: int = IN_F32_COPY
     order_mode: int = ORDER_REVERSE
     seed: int = 0
+    collective: int = ALL_REDUCE
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -74,9 +79,13 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """HBM bytes one full reduction pass must move: per element per
         replica 4 B read + 4 B write (fp32), or 2 B bf16 + 4 B fp32 read and
-        4 B write when bf16 wgrads are accumulated into fp32 main_grad."""
-        per = 10 if self.input_mode == IN_BF16_ACCUM_F32 else 8
-        return per * self.world * self.total_numel
+        4 B write when bf16 wgrads are accumulated into fp32 main_grad. A
+        reduce-scatter writes each element once (to its owner) instead of W
+        times."""
+        read = 6 if self.input_mode == IN_BF16_ACCUM_F32 else 4
+        if self.collective == REDUCE_SCATTER:
+            return (read * self.world + 4) * self.total_numel
+        return (read + 4) * self.world * self.total_numel
 
 
 def tiny() -> Workload:

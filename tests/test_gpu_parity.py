@@ -33,7 +33,7 @@ def say(*a):
 class Run:
     """Device inputs + reducer for a workload, on two torch streams."""
 
-    def __init__(self, wl, misalign=0, flat_shift=0, seed=None, same_stream=False):
+    def __init__(self, wl, misalign=0, flat_shift=0, seed=None, same_stream=False, collective=0):
         torch = _torch()
         import bucketed_gradient_all_amd as ddp
         from synth.device import DeviceInputs
@@ -48,8 +48,10 @@ class Run:
         self.compute = torch.cuda.Stream()
         self.comm = self.compute if same_stream else torch.cuda.Stream()
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
-                                  self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream)
+                                  self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
+                                  collective=collective)
         self.total = total
+        self.bucket_flat = [int(x) // 4 for x in bucket_flat]
 
     def step(self, order=None):
         ddp = self.ddp
@@ -368,3 +370,75 @@ def test_megatron_llama1b_bf16_accum_sampled_bit_exact():
 def test_sweep_sampled_bit_exact(W, cap_mib):
     from synth import workloads as wls
     _sampled(wls.sweep(W, cap_mib), per_param=4)
+
+
+# ------------------------------------------------------------ reduce-scatter
+def owned_mask(run, w):
+    """Flat positions replica w owns under reduce-scatter: chunk w of every bucket."""
+    mask = np.zeros(run.total, dtype=bool)
+    W = run.wl.world
+    for b in range(run.plan.n_buckets):
+        n = int(run.plan.bucket_bytes[b]) // 4
+        if n == 0:
+            continue
+        q = -(-n // W)
+        lo, hi = min(w * q, n), min((w + 1) * q, n)
+        base = run.bucket_flat[b]
+        mask[base + lo:base + hi] = True
+    return mask
+
+
+def check_reduce_scatter(run, before):
+    from expect import expected_flat, host_threads, oracle_plan
+    wl = run.wl
+    want = expected_flat(wl, oracle_plan(wl), wl.seed, nthreads=host_threads())
+    for w in range(wl.world):
+        got = run.flat_host(w)
+        m = owned_mask(run, w)
+        assert_bits(got[m], want[m], f"{wl.name} replica {w} owned shard")
+        assert_bits(got[~m], before[w][~m], f"{wl.name} replica {w} untouched part")
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 7, 8, 12, 16, 32])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_reduce_scatter_small_workloads_bit_exact(W, mode):
+    for seed in range(2):
+        wl = _small_workload(5000 + 1000 * W + 10 * mode + seed, W, mode)
+        say(f"case rs {wl.name} P={len(wl.numel)} cap={wl.cap_bytes}")
+        run = Run(wl, collective=1)
+        before = [run.flat_host(w) for w in range(W)]
+        run.step()
+        check_reduce_scatter(run, before)
+        run.close()
+
+
+def test_reduce_scatter_resnet50_full_bit_exact():
+    from synth import workloads as wls
+    wl = wls.resnet50()
+    run = Run(wl, collective=1)
+    before = [run.flat_host(w) for w in range(wl.world)]
+    say("resnet50 reduce-scatter")
+    run.step()
+    check_reduce_scatter(run, before)
+    run.close()
+
+
+def test_reduce_scatter_megatron_sampled_bit_exact():
+    """Owned shards of replica 0 and replica 15 at sampled elements."""
+    torch = _torch()
+    from synth import workloads as wls
+    from expect import expected_at, oracle_plan, sample_positions
+    wl = wls.megatron_llama1b()
+    run = Run(wl, collective=1)
+    say("megatron reduce-scatter")
+    run.step()
+    oplan = oracle_plan(wl)
+    pos = sample_positions(wl, oplan, 16, np.random.default_rng(3))
+    idx, want = expected_at(wl, oplan, pos, wl.seed)
+    for w in (0, wl.world - 1):
+        m = owned_mask(run, w)[idx]
+        sel = torch.from_numpy(idx[m]).to("cuda")
+        got = run.inputs.flat[w][sel].cpu().numpy()
+        assert m.sum() > 0
+        assert_bits(got, want[m], f"megatron rs replica {w}")
+    run.close()

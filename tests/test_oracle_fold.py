@@ -208,3 +208,35 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
         _fold().reduce_f32([np.zeros(3, np.float32), np.zeros(4, np.float32)])
     assert math.isfinite(float(_fold().reduce_f32([np.ones(1, np.float32)])[0]))
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8])
+def test_reduce_scatter_equals_literal_ring_reduce_scatter_phase(W):
+    """The value each chunk holds after the ring's reduce-scatter phase (the
+    rank that ends up with it, [DDP-ch17 §17.4]) is the reduce-scatter
+    result delivered to the replica that owns that shard [MegatronDDP §3]."""
+    from oracle.ring import ring_reduce_scatter
+    rng = np.random.default_rng(200 + W)
+    for n in (0, 1, 7, 16, 33, 67, 130):
+        x = _rand(rng, W, n)
+        rs = _fold().reduce_scatter_f32(x)
+        ring = ring_reduce_scatter(x)
+        for c in range(W):
+            lo, hi, vals = rs[c]
+            holder, rlo, rhi, rvals = ring[c]
+            assert (lo, hi) == (rlo, rhi) and holder == (c - 1) % W
+            np.testing.assert_array_equal(vals.view(np.uint32), rvals.view(np.uint32))
+
+
+def test_reduce_scatter_shards_tile_the_bucket_and_are_exact_on_a_dyadic_grid():
+    rng = np.random.default_rng(9)
+    W, n = 8, 1003
+    ks = rng.integers(-512, 513, size=(W, n))
+    x = [(ks[w] * 2.0 ** -10).astype(np.float32) for w in range(W)]
+    rs = _fold().reduce_scatter_f32(x)
+    assert rs[0][0] == 0 and rs[-1][1] == n
+    for c in range(1, W):
+        assert rs[c][0] == rs[c - 1][1]
+    exact = ks.sum(axis=0) * 2.0 ** -10 / W
+    for lo, hi, vals in rs:
+        np.testing.assert_array_equal(vals.astype(np.float64), exact[lo:hi])
