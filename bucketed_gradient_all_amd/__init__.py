@@ -81,6 +81,7 @@ class ddp_reducer_desc(ctypes.Structure):
         ("compute_stream", ctypes.c_void_p),
         ("comm_stream", ctypes.c_void_p),
         ("collective", ctypes.c_int32),
+        ("find_unused", ctypes.c_int32),
     ]
 
 
@@ -111,6 +112,8 @@ def lib():
             "ddp_get_launched": [P, P],
             "ddp_set_timing": [P, I32],
             "ddp_get_timings": [P, P, P, P, I32, P],
+            "ddp_set_require_sync": [P, I32],
+            "ddp_set_local_used": [P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -176,7 +179,7 @@ class Desc:
                  offset_in_bucket: Sequence[int], n_buckets: int, input_mode: int = DDP_IN_F32_COPY,
                  grads: Optional[Sequence[Sequence[int]]] = None, flat: Optional[Sequence[int]] = None,
                  workspace: int = 0, workspace_bytes: int = 0, compute_stream: int = 0, comm_stream: int = 0,
-                 collective: int = DDP_ALL_REDUCE):
+                 collective: int = DDP_ALL_REDUCE, find_unused: bool = False):
         self.numel = np.ascontiguousarray(param_numel, dtype=np.int64)
         self.bucket_of = np.ascontiguousarray(bucket_of, dtype=np.int32)
         self.offset = np.ascontiguousarray(offset_in_bucket, dtype=np.int64)
@@ -201,6 +204,7 @@ class Desc:
         d.compute_stream = compute_stream or None
         d.comm_stream = comm_stream or None
         d.collective = collective
+        d.find_unused = 1 if find_unused else 0
         self.c = d
 
     def set_workspace(self, ptr: int, nbytes: int) -> None:
@@ -254,6 +258,19 @@ def ddp_mark_ready_many(r: Reducer, params) -> int:
         err.n_done = done.value
         raise err
     return done.value
+
+
+def ddp_set_require_sync(r: Reducer, sync: bool) -> None:
+    _check(lib().ddp_set_require_sync(r.handle, 1 if sync else 0))
+
+
+def ddp_set_local_used(r: Reducer, used) -> None:
+    """used: [W, P] (or flat W*P) array, nonzero = replica used the gradient."""
+    arr = np.ascontiguousarray(np.asarray(used) != 0, dtype=np.uint8).reshape(-1)
+    W, P = r.desc.c.world, r.desc.numel.size
+    if arr.size != W * P:
+        raise ValueError(f"used table must have {W}*{P} entries")
+    _check(lib().ddp_set_local_used(r.handle, arr.ctypes.data))
 
 
 def ddp_bucket_reduce(r: Reducer, bucket: int, stream: int) -> None:
@@ -318,14 +335,15 @@ def ddp_get_timings(r: Reducer):
 
 def make_reducer(world: int, param_numel: Sequence[int], plan: BucketPlan, input_mode: int,
                  grad_ptrs: Optional[Sequence[Sequence[int]]], flat_ptrs: Sequence[int],
-                 compute_stream: int, comm_stream: int, collective: int = DDP_ALL_REDUCE) -> Reducer:
+                 compute_stream: int, comm_stream: int, collective: int = DDP_ALL_REDUCE,
+                 find_unused: bool = False) -> Reducer:
     """Creates a device reducer; the workspace is a torch allocation kept
     alive by the returned handle."""
     import torch
 
     desc = Desc(world, param_numel, plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, input_mode,
                 grads=grad_ptrs, flat=flat_ptrs, compute_stream=compute_stream, comm_stream=comm_stream,
-                collective=collective)
+                collective=collective, find_unused=find_unused)
     nbytes = ddp_workspace_bytes(desc)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     desc.set_workspace(ws.data_ptr(), nbytes)

@@ -25,7 +25,10 @@
 //   * fp32 adds and multiplies are issued as separate round-to-nearest
 //     operations (no contraction), so results equal the CPU oracle bit for bit.
 // The reduce-scatter variant (ZeRO-1 [MegatronDDP §3]) folds the same way but
-// stores chunk c only to replica c's flat buffer.
+// stores chunk c only to replica c's flat buffer. With unused-parameter
+// detection, a replica that did not use a gradient contributes a zero-filled
+// slice (its source is not read), and a gradient no replica used is left
+// untouched [DDP-ch17 §17.33].
 #include "internal.h"
 
 #include <hip/hip_runtime.h>
@@ -135,15 +138,24 @@ __device__ __forceinline__ const unsigned short *src_bf16(const KernelTables &T,
 
 // One element, any W: used for unaligned heads and tails and for segments
 // whose pointers do not allow 16-byte vectors.
+__device__ __forceinline__ uint64_t used_mask(const KernelTables &T, const DeviceSeg &sg)
+{
+    return T.used ? T.used[sg.param] : ~uint64_t(0);
+}
+
 template <int MODE>
 __device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t e, float s, int W, bool rs)
 {
+    const uint64_t m = used_mask(T, sg);
     float acc = 0.0f;
     for (int k = 0; k < W; ++k) {
         const int r = slot_replica(sg.chunk, k, W);
-        float x = ld1(src_f32<MODE>(T, sg, r) + e);
-        unsigned short g = MODE == MODE_BF16 ? ld1h(src_bf16(T, sg, r) + e) : 0;
-        float t = term1<MODE>(x, g, s);
+        float t = 0.0f;
+        if ((m >> r) & 1) {
+            float x = ld1(src_f32<MODE>(T, sg, r) + e);
+            unsigned short g = MODE == MODE_BF16 ? ld1h(src_bf16(T, sg, r) + e) : 0;
+            t = term1<MODE>(x, g, s);
+        }
         acc = k == 0 ? t : __fadd_rn(acc, t);
     }
     if (rs) {
@@ -176,13 +188,18 @@ __device__ __forceinline__ void scalar_parts(const KernelTables &T, const Device
 
 // One element with W known at compile time, from hoisted pointers; the sum
 // goes to the NOUT destinations (all W replicas, or the chunk's owner).
-template <int W, int NOUT, int MODE>
+template <int W, int NOUT, int MODE, bool USED>
 __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
-                                                  float *const (&ds)[NOUT], int64_t e, float s)
+                                                  float *const (&ds)[NOUT], const bool (&on)[W], int64_t e, float s)
 {
     float t[W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) t[k] = term1<MODE>(ld1(xs[k] + e), MODE == MODE_BF16 ? ld1h(gs[k] + e) : 0, s);
+    for (int k = 0; k < W; ++k) {
+        if (!USED || on[k])
+            t[k] = term1<MODE>(ld1(xs[k] + e), MODE == MODE_BF16 ? ld1h(gs[k] + e) : 0, s);
+        else
+            t[k] = 0.0f;
+    }
     float acc = t[0];
 #pragma unroll
     for (int k = 1; k < W; ++k) acc = __fadd_rn(acc, t[k]);
@@ -196,9 +213,10 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // then all stores. CHECK = true: the segment's last tile, with per-lane
 // bounds; out-of-range lanes load the segment's first vector (in bounds, value
 // unused) and skip their stores.
-template <int W, int NOUT, int MODE, bool CHECK>
+template <int W, int NOUT, int MODE, bool CHECK, bool USED>
 __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
-                                            float *const (&ds)[NOUT], const DeviceSeg &sg, int64_t tin, float s)
+                                            float *const (&ds)[NOUT], const bool (&on)[W], const DeviceSeg &sg,
+                                            int64_t tin, float s)
 {
     constexpr int U = unroll_for(W);
     constexpr int64_t TILE = tile_elems(W);
@@ -214,12 +232,22 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
     f32x4 v[U][W];
     u16x4 g[U][W];
 #pragma unroll
-    for (int k = 0; k < W; ++k)
+    for (int k = 0; k < W; ++k) {
+        if (USED && !on[k]) {
+            // a replica that did not use this gradient: zero-filled slice, not read
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                v[u][k] = f32x4{0, 0, 0, 0};
+                g[u][k] = u16x4{0, 0, 0, 0};
+            }
+            continue;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             v[u][k] = ld4(xs[k] + el[u]);
             g[u][k] = MODE == MODE_BF16 ? ld4h(gs[k] + el[u]) : u16x4{0, 0, 0, 0};
         }
+    }
     f32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -240,7 +268,7 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
 // the first store, so they stay in scalar registers; a table read after a
 // store would have to go through the vector memory path and wait for every
 // outstanding store.
-template <int W, int MODE, bool RS>
+template <int W, int MODE, bool RS, bool USED>
 __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, float s)
 {
     constexpr int NOUT = RS ? 1 : W;
@@ -266,24 +294,35 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
         for (int w = 0; w < NOUT; ++w) ds[w] = T.flat[w] + sg.flat;
     }
 
+    bool on[W];
+    if (USED) {
+        const uint64_t m = T.used[sg.param];
+        if (m == 0) return;   // no replica used this gradient: leave it untouched
+#pragma unroll
+        for (int k = 0; k < W; ++k) on[k] = (m >> slot_replica(sg.chunk, k, W)) & 1;
+    } else {
+#pragma unroll
+        for (int k = 0; k < W; ++k) on[k] = true;
+    }
+
     const int tid = int(threadIdx.x);
     if (sg.head >= 0) {
         if (sg.head + (tin + 1) * TILE <= sg.len)
-            vector_tile<W, NOUT, MODE, false>(xs, gs, ds, sg, tin, s);
+            vector_tile<W, NOUT, MODE, false, USED>(xs, gs, ds, on, sg, tin, s);
         else if (sg.len - sg.head >= 4)
-            vector_tile<W, NOUT, MODE, true>(xs, gs, ds, sg, tin, s);
+            vector_tile<W, NOUT, MODE, true, USED>(xs, gs, ds, on, sg, tin, s);
         if (tin == 0) {
             const int64_t body = (sg.len - sg.head) / 4 * 4;
             const int64_t tail = sg.len - sg.head - body;
-            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE>(xs, gs, ds, tid, s);
+            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE, USED>(xs, gs, ds, on, tid, s);
             if (tid >= 64 && tid < 64 + tail)
-                fold_scalar_fixed<W, NOUT, MODE>(xs, gs, ds, sg.head + body + (tid - 64), s);
+                fold_scalar_fixed<W, NOUT, MODE, USED>(xs, gs, ds, on, sg.head + body + (tid - 64), s);
         }
         return;
     }
     for (int64_t j = tid; j < TILE; j += kThreads) {
         const int64_t e = tin * TILE + j;
-        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE>(xs, gs, ds, e, s);
+        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, USED>(xs, gs, ds, on, e, s);
     }
 }
 
@@ -296,6 +335,8 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);
+    const uint64_t m = used_mask(T, sg);
+    if (m == 0) return;   // no replica used this gradient: leave it untouched
 
     if (sg.head >= 0) {
         for (int64_t e = sg.head + tin * TILE + int64_t(threadIdx.x) * 4; e < sg.head + (tin + 1) * TILE;
@@ -309,8 +350,13 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
                 for (int j = 0; j < 8; ++j) {
                     if (k0 + j < W) {
                         const int r = slot_replica(sg.chunk, k0 + j, W);
-                        v[j] = ld4(src_f32<MODE>(T, sg, r) + e);
-                        g[j] = MODE == MODE_BF16 ? ld4h(src_bf16(T, sg, r) + e) : u16x4{0, 0, 0, 0};
+                        if ((m >> r) & 1) {
+                            v[j] = ld4(src_f32<MODE>(T, sg, r) + e);
+                            g[j] = MODE == MODE_BF16 ? ld4h(src_bf16(T, sg, r) + e) : u16x4{0, 0, 0, 0};
+                        } else {
+                            v[j] = f32x4{0, 0, 0, 0};
+                            g[j] = u16x4{0, 0, 0, 0};
+                        }
                     }
                 }
 #pragma unroll
@@ -334,10 +380,18 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
 template <int W, int MODE>
 hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, float s, bool rs, hipStream_t st)
 {
-    if (rs)
-        hipLaunchKernelGGL((reduce_fixed<W, MODE, true>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s);
-    else
-        hipLaunchKernelGGL((reduce_fixed<W, MODE, false>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, s);
+    const dim3 g(n_tiles), b(kThreads);
+    if (t.used) {
+        if (rs)
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, true, true>), g, b, 0, st, t, tile_begin, s);
+        else
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, false, true>), g, b, 0, st, t, tile_begin, s);
+    } else {
+        if (rs)
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, true, false>), g, b, 0, st, t, tile_begin, s);
+        else
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, false, false>), g, b, 0, st, t, tile_begin, s);
+    }
     return hipGetLastError();
 }
 

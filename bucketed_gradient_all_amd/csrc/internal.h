@@ -43,12 +43,16 @@ struct KernelTables {
     const int32_t *tile_seg;       // tile -> segment
     const void *const *grads;      // [W*P] replica-major source pointers (COPY, BF16_ACCUM)
     float *const *flat;            // [W] flat buffers
+    const uint64_t *used;          // [P] bit w: replica w contributes gradient p (unused detection), or null
     int32_t n_params;
 };
 
 // Enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on stream s:
 // all-reduce (the sum stored to every replica) or reduce-scatter (chunk c
 // stored to replica c only). Returns hipSuccess or the launch error.
+// With t.used set, a replica whose bit is clear contributes a zero-filled
+// slice (its source is not read) and a gradient no replica used is not
+// written at all.
 hipError_t launch_bucket_reduce(int mode, int W, bool reduce_scatter, float scale, const KernelTables &t,
                                 int32_t tile_begin, int32_t n_tiles, hipStream_t s);
 

@@ -60,6 +60,7 @@ size_t align_up(size_t x)
 struct PlanView {
     int32_t W = 0, P = 0, B = 0, mode = 0;
     bool reduce_scatter = false;
+    bool find_unused = false;
     std::vector<int64_t> numel;
     std::vector<int32_t> bucket_of;
     std::vector<int64_t> offset;                 // bytes inside the bucket
@@ -137,6 +138,8 @@ int validate(const ddp_reducer_desc *d, PlanView &pv)
         return fail(DDP_ERR_INVALID, "unknown input mode");
     if (d->collective != DDP_ALL_REDUCE && d->collective != DDP_REDUCE_SCATTER)
         return fail(DDP_ERR_INVALID, "unknown collective");
+    if (d->find_unused && d->world > 64)
+        return fail(DDP_ERR_INVALID, "unused-parameter detection supports at most 64 replicas");
     if (d->n_params > 0 && (!d->param_numel || !d->bucket_of || !d->offset_in_bucket))
         return fail(DDP_ERR_INVALID, "plan arrays are NULL");
     pv.W = d->world;
@@ -144,6 +147,7 @@ int validate(const ddp_reducer_desc *d, PlanView &pv)
     pv.B = d->n_buckets;
     pv.mode = d->input_mode;
     pv.reduce_scatter = d->collective == DDP_REDUCE_SCATTER;
+    pv.find_unused = d->find_unused != 0;
     pv.numel.assign(d->param_numel, d->param_numel + pv.P);
     pv.bucket_of.assign(d->bucket_of, d->bucket_of + pv.P);
     pv.offset.assign(d->offset_in_bucket, d->offset_in_bucket + pv.P);
@@ -181,7 +185,7 @@ int validate(const ddp_reducer_desc *d, PlanView &pv)
 }
 
 struct Layout {
-    size_t grads_off = 0, flat_off = 0, segs_off = 0, tiles_off = 0, total = 0;
+    size_t grads_off = 0, flat_off = 0, segs_off = 0, tiles_off = 0, used_off = 0, total = 0;
 };
 
 Layout layout_of(const PlanView &pv)
@@ -196,6 +200,8 @@ Layout layout_of(const PlanView &pv)
     cur = align_up(cur + sizeof(DeviceSeg) * pv.segs.size());
     l.tiles_off = cur;
     cur = align_up(cur + sizeof(int32_t) * pv.tile_seg.size());
+    l.used_off = cur;
+    if (pv.find_unused) cur = align_up(cur + sizeof(uint64_t) * size_t(pv.P));
     l.total = cur;
     return l;
 }
@@ -215,6 +221,17 @@ struct ddp_reducer {
     std::vector<int32_t> timed_count;     // buckets covered by each recorded launch
     ddp_comm_hook_fn hook = nullptr;
     void *hook_ctx = nullptr;
+    // unused-parameter detection and no_sync [DDP-ch17 §17.33; PTD-notes §2.2.3, §2.2.4]
+    bool require_sync = true;             // read at the next prepare
+    bool sync = true;                     // this backward reduces
+    std::vector<uint8_t> window;          // [W*P] OR of the used tables since the last synchronized pass
+    bool window_set = false;
+    std::vector<uint64_t> masks;          // [P] bit w: replica w contributes gradient p
+    bool masks_uploaded = false;
+    uint64_t *stage = nullptr;            // pinned host staging, 2 slots of P masks
+    hipEvent_t stage_ev[2] = {nullptr, nullptr};
+    int stage_slot = 0;
+    uint64_t *used_dev = nullptr;         // device masks inside the workspace
     // per-iteration state [DDP-ch17 §17.12, §17.16]
     std::vector<int32_t> pending;
     std::vector<uint8_t> ready;
@@ -225,6 +242,7 @@ struct ddp_reducer {
 
     void reset()
     {
+        masks_uploaded = false;
         pending.resize(pv.B);
         for (int b = 0; b < pv.B; ++b) pending[b] = int32_t(pv.members[b].size());
         ready.assign(pv.P, 0);
@@ -240,7 +258,18 @@ struct ddp_reducer {
             if (!ready[p]) out.push_back(p);
         return out;
     }
-    bool in_iteration() const { return marks > 0 && !finished; }
+    bool in_iteration() const { return sync && marks > 0 && !finished; }
+
+    // the per-gradient replica masks of this synchronization window
+    void compute_masks()
+    {
+        const uint64_t all = pv.W >= 64 ? ~uint64_t(0) : ((uint64_t(1) << pv.W) - 1);
+        masks.assign(pv.P, window_set ? 0 : all);
+        if (!window_set) return;
+        for (int w = 0; w < pv.W; ++w)
+            for (int32_t p = 0; p < pv.P; ++p)
+                if (window[size_t(w) * pv.P + p]) masks[p] |= uint64_t(1) << w;
+    }
 };
 
 namespace {
@@ -285,6 +314,25 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
 // [PTD-notes §2.3; MegatronDDP §3]. When the compute stream has already
 // drained, every gradient it produced is complete and visible, so the
 // cross-stream event (a few microseconds of queue latency) is skipped.
+// The replica masks of this backward go to the device once, on the comm
+// stream, ahead of its first reduction: the per-replica "used" tables reduced
+// over replicas (a bitwise OR) [DDP-ch17 §17.33; PTD-notes §3.2].
+int upload_masks(ddp_reducer *r)
+{
+    if (!r->pv.find_unused || !r->device || r->masks_uploaded || r->pv.P == 0) return DDP_OK;
+    const int slot = r->stage_slot;
+    r->stage_slot ^= 1;
+    hipError_t e = hipEventSynchronize(r->stage_ev[slot]);   // the copy that last used this slot is done
+    if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+    uint64_t *h = r->stage + size_t(slot) * r->pv.P;
+    std::copy(r->masks.begin(), r->masks.end(), h);
+    e = hipMemcpyAsync(r->used_dev, h, sizeof(uint64_t) * r->pv.P, hipMemcpyHostToDevice, r->comm);
+    if (e == hipSuccess) e = hipEventRecord(r->stage_ev[slot], r->comm);
+    if (e != hipSuccess) return hip_fail("mask upload", e);
+    r->masks_uploaded = true;
+    return DDP_OK;
+}
+
 int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
 {
     if (b0 >= b1) return DDP_OK;
@@ -296,6 +344,8 @@ int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
         }
         if (e != hipSuccess) return hip_fail("stream wait", e);
     }
+    int urc = upload_masks(r);
+    if (urc != DDP_OK) return urc;
     if (r->hook) {
         for (int32_t b = b0; b < b1; ++b) {
             int rc = r->hook(r->hook_ctx, b);
@@ -311,22 +361,43 @@ int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
 // One gradient-ready mark [DDP-ch17 §17.12]: advances r->next past every
 // bucket that is now launchable, in index order [L15 §2.3]; the caller
 // launches [old next, new next).
-int mark_one(ddp_reducer *r, int32_t param)
+void mark_state(ddp_reducer *r, int32_t param)
 {
-    if (param < 0 || param >= r->pv.P) return fail(DDP_ERR_INVALID, "gradient index out of range");
-    if (r->ready[param])
-        return fail(DDP_ERR_ALREADY_READY,
-                    "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
     r->ready[param] = 1;
     r->ready_order.push_back(param);
     ++r->marks;
     --r->pending[r->pv.bucket_of[param]];
+}
+
+int mark_one(ddp_reducer *r, int32_t param)
+{
+    if (param < 0 || param >= r->pv.P) return fail(DDP_ERR_INVALID, "gradient index out of range");
+    if (!r->sync) return DDP_OK;   // hooks are disabled inside no_sync [L15 §4.1; PTD-notes §2.2.4]
+    if (r->marks == 0 && r->pv.find_unused) {
+        // first hook of the backward: gradients no replica used are ready now
+        // [DDP-ch17 §17.33]
+        r->compute_masks();
+        for (int32_t q = 0; q < r->pv.P; ++q)
+            if (r->masks[q] == 0 && q != param) mark_state(r, q);
+    }
+    if (r->ready[param])
+        return fail(DDP_ERR_ALREADY_READY,
+                    "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
+    mark_state(r, param);
     while (r->next < r->pv.B && r->pending[r->next] == 0) ++r->next;
     return DDP_OK;
 }
 
 void destroy_events(ddp_reducer *r)
 {
+    for (auto &ev : r->stage_ev)
+        if (ev) {
+            (void)hipEventSynchronize(ev);
+            (void)hipEventDestroy(ev);
+            ev = nullptr;
+        }
+    if (r->stage) (void)hipHostFree(r->stage);
+    r->stage = nullptr;
     if (r->ev_ready) (void)hipEventDestroy(r->ev_ready);
     if (r->ev_done) (void)hipEventDestroy(r->ev_done);
     for (auto e : r->t0)
@@ -410,7 +481,7 @@ size_t ddp_workspace_bytes(const ddp_reducer_desc *desc)
 {
     PlanView pv;
     if (validate(desc, pv) != DDP_OK) return 0;
-    if (build_segments(pv, pv.mode != DDP_IN_F32_VIEW) != DDP_OK) return 0;
+    if (build_segments(pv, pv.mode != DDP_IN_F32_VIEW || pv.find_unused) != DDP_OK) return 0;
     return layout_of(pv).total;
 }
 
@@ -431,7 +502,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
     r->comm = static_cast<hipStream_t>(desc->comm_stream);
     if (r->device) {
         const bool copy_src = pv.mode != DDP_IN_F32_VIEW;
-        rc = build_segments(pv, copy_src);
+        rc = build_segments(pv, copy_src || pv.find_unused);
         if (rc != DDP_OK) {
             delete r;
             return rc;
@@ -498,6 +569,10 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         std::memcpy(host.data() + lay.flat_off, desc->flat, sizeof(float *) * size_t(pv.W));
         std::memcpy(host.data() + lay.segs_off, pv.segs.data(), sizeof(DeviceSeg) * pv.segs.size());
         std::memcpy(host.data() + lay.tiles_off, pv.tile_seg.data(), sizeof(int32_t) * pv.tile_seg.size());
+        if (pv.find_unused) {
+            r->compute_masks();   // nothing recorded yet: every replica contributes
+            std::memcpy(host.data() + lay.used_off, r->masks.data(), sizeof(uint64_t) * pv.P);
+        }
         hipError_t e = hipMemcpy(desc->workspace, host.data(), lay.total, hipMemcpyHostToDevice);
         if (e != hipSuccess) {
             delete r;
@@ -509,14 +584,24 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         r->tables.segs = reinterpret_cast<const DeviceSeg *>(ws + lay.segs_off);
         r->tables.tile_seg = reinterpret_cast<const int32_t *>(ws + lay.tiles_off);
         r->tables.n_params = pv.P;
+        if (pv.find_unused) {
+            r->used_dev = reinterpret_cast<uint64_t *>(ws + lay.used_off);
+            r->tables.used = r->used_dev;
+        }
         e = hipEventCreateWithFlags(&r->ev_ready, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_done, hipEventDisableTiming);
+        if (e == hipSuccess && pv.find_unused && pv.P > 0) {
+            e = hipHostMalloc(reinterpret_cast<void **>(&r->stage), 2 * sizeof(uint64_t) * pv.P);
+            for (int k = 0; k < 2 && e == hipSuccess; ++k)
+                e = hipEventCreateWithFlags(&r->stage_ev[k], hipEventDisableTiming);
+        }
         if (e != hipSuccess) {
             destroy_events(r);
             delete r;
             return hip_fail("hipEventCreate", e);
         }
     }
+    if (pv.find_unused) r->window.assign(size_t(pv.W) * pv.P, 0);
     r->reset();
     *out = r;
     return DDP_OK;
@@ -538,6 +623,7 @@ int ddp_prepare_for_backward(ddp_reducer *r)
                     "the previous iteration's reduction never finished before a new one was prepared; "
                     "gradients never marked ready: " + list_params(r->unready()));
     r->reset();
+    r->sync = r->require_sync;
     return DDP_OK;
 }
 
@@ -584,6 +670,24 @@ int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream)
 int ddp_finish(ddp_reducer *r, int32_t host_blocking)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (!r->sync) {           // no_sync: nothing was reduced, the used tables keep accumulating
+        r->finished = true;
+        return DDP_OK;
+    }
+    if (r->pv.find_unused && r->marks == 0 && r->next < r->pv.B) {
+        // a backward in which no hook fired: every gradient unused everywhere
+        // still completes, as at a first hook
+        r->compute_masks();
+        bool all_unused = true;
+        for (uint64_t m : r->masks) all_unused &= m == 0;
+        if (all_unused) {
+            const int32_t b0 = r->next;
+            for (int32_t q = 0; q < r->pv.P; ++q) mark_state(r, q);
+            while (r->next < r->pv.B && r->pending[r->next] == 0) ++r->next;
+            int lrc = launch_buckets(r, b0, r->next);
+            if (lrc != DDP_OK) return lrc;
+        }
+    }
     if (r->next < r->pv.B)
         return fail(DDP_ERR_NOT_READY,
                     "buckets still wait for gradients never marked ready: " + list_params(r->unready()));
@@ -594,6 +698,29 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
         if (e != hipSuccess) return hip_fail("finish", e);
     }
     r->finished = true;
+    if (r->pv.find_unused) {
+        std::fill(r->window.begin(), r->window.end(), 0);
+        r->window_set = false;
+    }
+    return DDP_OK;
+}
+
+int ddp_set_require_sync(ddp_reducer *r, int32_t sync)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    r->require_sync = sync != 0;
+    return DDP_OK;
+}
+
+int ddp_set_local_used(ddp_reducer *r, const uint8_t *used)
+{
+    if (!r || !used) return fail(DDP_ERR_INVALID, "NULL argument");
+    if (!r->pv.find_unused) return fail(DDP_ERR_INVALID, "unused-parameter detection is off for this reducer");
+    if (r->sync && r->marks > 0)
+        return fail(DDP_ERR_INVALID, "the used table must be set before the first gradient of the backward");
+    for (size_t i = 0; i < r->window.size(); ++i)
+        if (used[i]) r->window[i] = 1;
+    r->window_set = true;
     return DDP_OK;
 }
 

@@ -140,6 +140,8 @@ typedef struct {
     void *comm_stream;                 /* hipStream_t on which bucket reductions run (a side
                                           stream that overlaps backward [PTD-notes §2.3])           */
     int32_t collective;                /* DDP_ALL_REDUCE (0) or DDP_REDUCE_SCATTER                  */
+    int32_t find_unused;               /* != 0: per-replica used tables (ddp_set_local_used) decide
+                                          which gradients contribute; W <= 64 [DDP-ch17 §17.33]     */
 } ddp_reducer_desc;
 
 /* Device workspace the reducer needs for its tables (segments, tiles,
@@ -203,6 +205,30 @@ int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
  * ready), then makes the compute stream wait for the comm stream; with
  * host_blocking != 0 the host also waits for the reductions to complete. */
 int ddp_finish(ddp_reducer *r, int32_t host_blocking);
+
+/* no_sync [L15 §4.1; PTD-notes §2.2.4]: with sync == 0, the backward passes
+ * prepared from now on do not reduce: ddp_mark_ready only checks the index,
+ * ddp_finish does nothing, and gradients are left to accumulate locally in
+ * the caller's buffers; the next backward prepared with sync != 0 reduces the
+ * accumulated sum. The flag is read by ddp_prepare_for_backward. Default 1. */
+int ddp_set_require_sync(ddp_reducer *r, int32_t sync);
+
+/* Unused-parameter detection (desc.find_unused) [DDP-ch17 §17.33; L15 §4.2;
+ * PTD-notes §2.2.3, §3.2]. used: [W*P] host bytes, entry w*P + p != 0 when
+ * replica w produced gradient p in this backward. Call after
+ * ddp_prepare_for_backward and before the backward's first ddp_mark_ready.
+ * Tables OR together over every backward since the last synchronized one
+ * (no_sync passes included). In the next synchronized backward:
+ *  - at the first ready mark, gradients no replica used are marked ready;
+ *  - a replica that did not use gradient p contributes a zero-filled slice
+ *    (its source is not read);
+ *  - gradients no replica used are not written (their flat-buffer slices keep
+ *    their contents).
+ * The reduced tables go to the device once per synchronized backward, on the
+ * comm stream, ahead of its first reduction. Without a call every replica
+ * counts as having used every gradient. Errors: DDP_ERR_INVALID if detection
+ * is off or the backward already started. */
+int ddp_set_local_used(ddp_reducer *r, const uint8_t *used);
 
 /* Replaces the default hook [DDP-ch17 §17.9, §17.20; L15 §2.2]: fn(ctx, b)
  * is called for each bucket launch, in launch order, after the comm stream

@@ -18,6 +18,19 @@ What the pages fix:
   * the end of backward waits for every bucket's collective
     [DDP-ch17 §17.41; MegatronDDP §2, §5].
 
+Skipping synchronization and unused parameters:
+  * inside no_sync the hooks are disabled: backward passes only accumulate
+    gradients locally, and the next synchronized backward reduces the sum;
+    the flag is read when the backward is prepared [L15 §4.1; PTD-notes
+    §2.2.4];
+  * with unused-parameter detection, parameters no replica used are marked
+    ready at the first hook of the backward; a replica that did not use a
+    parameter contributes a zero-filled slice; the per-replica "used" tables
+    are reduced separately, and parameters no replica used keep their
+    gradient untouched [DDP-ch17 §17.33; L15 §4.2; PTD-notes §2.2.3, §3.2];
+  * the used tables keep accumulating through no_sync passes until the next
+    synchronized one [PTD-notes §2.2.4].
+
 Reading: finishing an iteration whose buckets have not all launched is an
 error that lists, in ascending order, the parameters not marked ready.
 
@@ -45,9 +58,12 @@ class ModelError(Exception):
 
 
 class ReducerModel:
-    def __init__(self, buckets: Sequence[Sequence[int]], n_params: int):
+    def __init__(self, buckets: Sequence[Sequence[int]], n_params: int, world: int = 1,
+                 find_unused: bool = False):
         self.buckets = [list(b) for b in buckets]
         self.P = n_params
+        self.W = world
+        self.find_unused = find_unused
         self.bucket_of = [-1] * n_params
         for b, members in enumerate(self.buckets):
             for p in members:
@@ -55,7 +71,10 @@ class ReducerModel:
         if any(b < 0 for b in self.bucket_of):
             raise ModelError(ERR_INVALID)
         self.launched: List[int] = []      # every launch since construction
+        self.require_sync = True
+        self.window_used = None            # [W][P] OR of used tables since the last synchronized pass
         self._reset()
+        self.sync = True
 
     def _reset(self) -> None:
         self.pending = [len(m) for m in self.buckets]
@@ -68,21 +87,56 @@ class ReducerModel:
     def _unready(self) -> List[int]:
         return [p for p in range(self.P) if not self.ready[p]]
 
+    def set_require_sync(self, flag: bool) -> None:
+        self.require_sync = bool(flag)
+
     def prepare_for_backward(self) -> None:
-        if self.marks > 0 and not self.finished:
+        if self.sync and self.marks > 0 and not self.finished:
             raise ModelError(ERR_UNFINISHED, self._unready())
         self._reset()
+        self.sync = self.require_sync
+
+    def set_local_used(self, used: Sequence[Sequence[int]]) -> None:
+        """used[w][p] != 0: replica w produced a gradient for p in this pass."""
+        if not self.find_unused or self.marks > 0:
+            raise ModelError(ERR_INVALID)
+        if self.window_used is None:
+            self.window_used = [[0] * self.P for _ in range(self.W)]
+        for w in range(self.W):
+            for p in range(self.P):
+                if used[w][p]:
+                    self.window_used[w][p] = 1
+
+    def used_mask(self) -> List[List[int]]:
+        """Per replica and parameter: 1 if it contributes its gradient, 0 if
+        its slice counts as zero (all 1 without unused detection)."""
+        if self.window_used is None:
+            return [[1] * self.P for _ in range(self.W)]
+        return [row[:] for row in self.window_used]
+
+    def globally_unused(self) -> List[int]:
+        m = self.used_mask()
+        return [p for p in range(self.P) if not any(m[w][p] for w in range(self.W))]
+
+    def _mark(self, p: int) -> None:
+        self.ready[p] = True
+        self.marks += 1
+        self.ready_order.append(p)
+        self.pending[self.bucket_of[p]] -= 1
 
     def mark_ready(self, p: int) -> List[int]:
         """Returns the buckets this call launches, in launch order."""
         if not 0 <= p < self.P:
             raise ModelError(ERR_INVALID)
+        if not self.sync:
+            return []                     # hooks are disabled inside no_sync
         if self.ready[p]:
             raise ModelError(ERR_ALREADY_READY, [p])
-        self.ready[p] = True
-        self.marks += 1
-        self.ready_order.append(p)
-        self.pending[self.bucket_of[p]] -= 1
+        if self.marks == 0 and self.find_unused:
+            for q in self.globally_unused():
+                if q != p:
+                    self._mark(q)
+        self._mark(p)
         out = []
         while self.next_bucket < len(self.buckets) and self.pending[self.next_bucket] == 0:
             out.append(self.next_bucket)
@@ -90,10 +144,25 @@ class ReducerModel:
         self.launched += out
         return out
 
-    def finish(self) -> None:
+    def finish(self) -> List[int]:
+        """Returns the buckets launched by finishing (only in a backward where
+        no hook fired and no replica used any gradient)."""
+        if not self.sync:
+            self.finished = True
+            return []
+        out = []
+        if self.find_unused and self.marks == 0 and len(self.globally_unused()) == self.P:
+            for q in range(self.P):
+                self._mark(q)
+            while self.next_bucket < len(self.buckets) and self.pending[self.next_bucket] == 0:
+                out.append(self.next_bucket)
+                self.next_bucket += 1
+            self.launched += out
         if self.next_bucket < len(self.buckets):
             raise ModelError(ERR_NOT_READY, self._unready())
         self.finished = True
+        self.window_used = None
+        return out
 
 
 def comm_timeline(bucket_bytes: Sequence[float], bucket_ready: Sequence[float], alpha: float,

@@ -25,9 +25,10 @@ def _scale(wl):
     return synth.scale_for(wl.dist, wl.sigma)
 
 
-def bucket_inputs(wl: Workload, plan, b: int, seed: int):
+def bucket_inputs(wl: Workload, plan, b: int, seed: int, used=None):
     """Per-replica inputs of bucket b in flat order: fp32 arrays (and bf16
-    wgrad arrays in the bf16 mode)."""
+    wgrad arrays in the bf16 mode). used[w][p] == 0: replica w's slice of p
+    is zero-filled (unused-parameter detection)."""
     members = plan.buckets[b]
     n = plan.bucket_bytes[b] // 4
     sc = _scale(wl)
@@ -38,6 +39,11 @@ def bucket_inputs(wl: Workload, plan, b: int, seed: int):
         for p in members:
             o = plan.offset_in_bucket[p] // 4
             m = wl.numel[p]
+            if used is not None and not used[w][p]:
+                x[o:o + m] = 0.0
+                if g is not None:
+                    g[o:o + m] = 0
+                continue
             if wl.input_mode == IN_BF16_ACCUM_F32:
                 x[o:o + m] = synth.host_f32(synth.key(seed, STREAM_MAIN, w, p), wl.dist, sc, m)
                 g[o:o + m] = synth.host_bf16(synth.key(seed, STREAM_WGRAD, w, p), wl.dist, sc, m)
@@ -48,20 +54,27 @@ def bucket_inputs(wl: Workload, plan, b: int, seed: int):
     return xs, gs
 
 
-def expected_bucket(wl: Workload, plan, b: int, seed: int, nthreads: int = 0) -> np.ndarray:
-    xs, gs = bucket_inputs(wl, plan, b, seed)
+def expected_bucket(wl: Workload, plan, b: int, seed: int, nthreads: int = 0, used=None) -> np.ndarray:
+    xs, gs = bucket_inputs(wl, plan, b, seed, used)
     if wl.input_mode == IN_BF16_ACCUM_F32:
         return fold.reduce_bf16acc(xs, gs, nthreads=nthreads)
     return fold.reduce_f32(xs, nthreads=nthreads)
 
 
-def expected_flat(wl: Workload, plan, seed: int, nthreads: int = 0) -> np.ndarray:
+def expected_flat(wl: Workload, plan, seed: int, nthreads: int = 0, used=None) -> np.ndarray:
     total = sum(plan.bucket_bytes) // 4
     out = np.empty(total, np.float32)
     for b in range(plan.n_buckets):
         o = plan.bucket_offset[b] // 4
-        out[o:o + plan.bucket_bytes[b] // 4] = expected_bucket(wl, plan, b, seed, nthreads)
+        out[o:o + plan.bucket_bytes[b] // 4] = expected_bucket(wl, plan, b, seed, nthreads, used)
     return out
+
+
+def param_flat_ranges(wl: Workload, plan):
+    """(start, end) flat element range of every gradient."""
+    return [(plan.bucket_offset[plan.bucket_of[p]] // 4 + plan.offset_in_bucket[p] // 4,
+             plan.bucket_offset[plan.bucket_of[p]] // 4 + plan.offset_in_bucket[p] // 4 + wl.numel[p])
+            for p in range(len(wl.numel))]
 
 
 def sample_positions(wl: Workload, plan, per_param: int, rng: np.random.Generator) -> List[Tuple[int, int]]:

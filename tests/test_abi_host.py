@@ -314,3 +314,59 @@ def test_mark_ready_many_launches_completed_buckets_before_reporting_an_error():
         ddp.ddp_mark_ready_many(r, [7, 6, 5, 5])
     assert e.value.code == ddp.DDP_ERR_ALREADY_READY and e.value.n_done == 3
     assert log == [0]
+
+
+def host_reducer_unused(numel, cap, first, W):
+    pb = [4 * n for n in numel]
+    plan = ddp.ddp_plan_buckets(pb, ddp.DDP_ORDER_REVERSE, cap, first)
+    desc = ddp.Desc(W, numel, plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, find_unused=True)
+    r = ddp.ddp_reducer_create(desc)
+    log = []
+    ddp.ddp_register_comm_hook(r, lambda b: log.append(b) or 0)
+    return r, plan, log
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_no_sync_and_unused_state_machine_matches_oracle(seed):
+    rng = random.Random(seed)
+    W = rng.choice([1, 2, 4, 8])
+    P = rng.randint(1, 20)
+    numel = [rng.randint(1, 30) for _ in range(P)]
+    r, plan, log = host_reducer_unused(numel, rng.choice([16, 64, 400]), 16, W)
+    model = ReducerModel(plan.buckets(), P, world=W, find_unused=True)
+    for it in range(6):
+        sync = rng.random() < 0.6
+        ddp.ddp_set_require_sync(r, sync)
+        model.set_require_sync(sync)
+        ddp.ddp_prepare_for_backward(r)
+        model.prepare_for_backward()
+        used = [[1 if rng.random() < 0.7 else 0 for _ in range(P)] for _ in range(W)]
+        if rng.random() < 0.8:
+            ddp.ddp_set_local_used(r, used)
+            model.set_local_used(used)
+        unused_now = set(model.globally_unused()) if sync else set()
+        order = [p for p in range(P) if p not in unused_now]
+        rng.shuffle(order)
+        for p in order:
+            before = len(log)
+            ddp.ddp_mark_ready(r, p)
+            assert log[before:] == model.mark_ready(p)
+        before = len(log)
+        ddp.ddp_finish(r)
+        assert log[before:] == model.finish()
+    assert log == model.launched
+
+
+def test_local_used_errors():
+    r, plan, log = host_reducer([4, 4], 16, 16)          # detection off
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_set_local_used(r, [[1, 1], [1, 1]])
+    assert e.value.code == ddp.DDP_ERR_INVALID
+    r, plan, log = host_reducer_unused([4, 4], 16, 16, 2)
+    ddp.ddp_set_local_used(r, [[1, 1], [1, 1]])
+    ddp.ddp_mark_ready(r, 1)
+    with pytest.raises(ddp.DDPError) as e:              # the backward has started
+        ddp.ddp_set_local_used(r, [[1, 1], [1, 1]])
+    assert e.value.code == ddp.DDP_ERR_INVALID
+    with pytest.raises(ddp.DDPError):                   # more than 64 replicas
+        ddp.ddp_reducer_create(ddp.Desc(65, [4], [0], [0], 1, find_unused=True))

@@ -1,0 +1,150 @@
+"""GPU parity for unused-parameter detection and no_sync: per-replica used
+tables decide which slices contribute (zero-filled otherwise) and gradients
+no replica used keep their flat-buffer contents [DDP-ch17 §17.33; L15 §4.1,
+§4.2]. All comparisons bit for bit against the CPU oracle."""
+import random
+
+import numpy as np
+import pytest
+
+from test_gpu_parity import Run, _small_workload, _torch, assert_bits, owned_mask, say
+
+pytestmark = pytest.mark.gpu
+
+
+class URun(Run):
+    def __init__(self, wl, collective=0):
+        torch = _torch()
+        import bucketed_gradient_all_amd as ddp
+        from synth.device import DeviceInputs
+        self.torch, self.ddp, self.wl = torch, ddp, wl
+        self.plan = ddp.ddp_plan_buckets(wl.param_bytes, wl.order_mode, wl.cap_bytes, wl.first_cap_bytes)
+        bb = [int(x) for x in self.plan.bucket_bytes]
+        bucket_flat = np.concatenate([[0], np.cumsum(bb)])[:-1] if bb else np.zeros(0, np.int64)
+        flat_off = [int(bucket_flat[self.plan.bucket_of[p]] + self.plan.offset_in_bucket[p]) // 4
+                    for p in range(len(wl.numel))]
+        self.total = sum(bb) // 4
+        self.bucket_flat = [int(x) // 4 for x in bucket_flat]
+        self.inputs = DeviceInputs(wl, flat_off, self.total)
+        self.compute = torch.cuda.Stream()
+        self.comm = torch.cuda.Stream()
+        self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
+                                  self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
+                                  collective=collective, find_unused=True)
+
+
+def random_used(rng, W, P, p_unused=0.3, p_global=0.2):
+    used = [[1 if rng.random() > p_unused else 0 for _ in range(P)] for _ in range(W)]
+    for p in range(P):
+        if rng.random() < p_global:
+            for w in range(W):
+                used[w][p] = 0
+    return used
+
+
+def check(run, used, before, collective=0):
+    from expect import expected_flat, host_threads, oracle_plan, param_flat_ranges
+    wl = run.wl
+    oplan = oracle_plan(wl)
+    want = expected_flat(wl, oplan, wl.seed, nthreads=host_threads(), used=used)
+    untouched = np.zeros(run.total, dtype=bool)
+    for p, (lo, hi) in enumerate(param_flat_ranges(wl, oplan)):
+        if not any(used[w][p] for w in range(wl.world)):
+            untouched[lo:hi] = True
+    for w in range(wl.world):
+        got = run.flat_host(w)
+        owned = owned_mask(run, w) if collective else np.ones(run.total, dtype=bool)
+        m = owned & ~untouched
+        assert_bits(got[m], want[m], f"{wl.name} replica {w} reduced part")
+        assert_bits(got[~m], before[w][~m], f"{wl.name} replica {w} untouched part")
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 12, 16])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("collective", [0, 1])
+def test_unused_slices_are_zero_and_globally_unused_untouched(W, mode, collective):
+    rng = random.Random(100 * W + 10 * mode + collective)
+    wl = _small_workload(9000 + 100 * W + 10 * mode + collective, W, mode)
+    P = len(wl.numel)
+    say(f"case unused {wl.name} P={P} collective={collective}")
+    run = URun(wl, collective)
+    used = random_used(rng, W, P)
+    before = [run.flat_host(w) for w in range(W)]
+    ddp = run.ddp
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_set_local_used(run.r, used)
+    unused_everywhere = {p for p in range(P) if not any(used[w][p] for w in range(W))}
+    order = [p for p in range(P - 1, -1, -1) if p not in unused_everywhere]
+    for p in order:
+        ddp.ddp_mark_ready(run.r, p)
+    ddp.ddp_finish(run.r, host_blocking=True)
+    check(run, used, before, collective)
+    run.close()
+
+
+def test_no_sync_accumulates_used_tables_and_reduces_once():
+    """Two no_sync passes launch nothing; the synchronized pass reduces with
+    the OR of the three passes' used tables."""
+    torch = _torch()
+    from synth import workloads as wls
+    wl = wls.tiny()
+    W, P = wl.world, len(wl.numel)
+    run = URun(wl)
+    ddp = run.ddp
+    rng = random.Random(4)
+    tables = [random_used(rng, W, P, 0.6, 0.0) for _ in range(3)]
+    before = [run.flat_host(w) for w in range(W)]
+    ddp.ddp_set_timing(run.r, True)
+    ddp.ddp_set_require_sync(run.r, False)
+    for k in range(2):
+        ddp.ddp_prepare_for_backward(run.r)
+        ddp.ddp_set_local_used(run.r, tables[k])
+        for p in range(P - 1, -1, -1):
+            ddp.ddp_mark_ready(run.r, p)
+        ddp.ddp_finish(run.r, host_blocking=True)
+    torch.cuda.synchronize()
+    assert len(ddp.ddp_get_timings(run.r)[0]) == 0
+    for w in range(W):
+        assert_bits(run.flat_host(w), before[w], "no_sync pass wrote")
+    ddp.ddp_set_require_sync(run.r, True)
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_set_local_used(run.r, tables[2])
+    used = [[int(any(t[w][p] for t in tables)) for p in range(P)] for w in range(W)]
+    unused_everywhere = {p for p in range(P) if not any(used[w][p] for w in range(W))}
+    ddp.ddp_mark_ready_many(run.r, [p for p in range(P - 1, -1, -1) if p not in unused_everywhere])
+    ddp.ddp_finish(run.r, host_blocking=True)
+    assert len(ddp.ddp_get_timings(run.r)[0]) >= 1
+    check(run, used, before)
+    # the next synchronized pass starts from a clean table: everything used
+    run.inputs.refill()
+    before = [run.flat_host(w) for w in range(W)]
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_mark_ready_many(run.r, list(range(P - 1, -1, -1)))
+    ddp.ddp_finish(run.r, host_blocking=True)
+    check(run, [[1] * P for _ in range(W)], before)
+    run.close()
+
+
+def test_resnet50_with_unused_branch_bit_exact():
+    """ResNet-50 shapes, W=8: the last stage's downsample branch unused on
+    every replica, the fc layer used on half of them."""
+    from synth import workloads as wls
+    wl = wls.resnet50()
+    P, W = len(wl.numel), wl.world
+    used = [[1] * P for _ in range(W)]
+    ds = [p for p, s in enumerate(wl.shapes) if s == (2048, 1024, 1, 1)]   # stage-4 projection conv
+    for p in ds + [ds[0] + 1, ds[0] + 2]:
+        for w in range(W):
+            used[w][p] = 0
+    for w in range(W // 2):
+        used[w][P - 1] = used[w][P - 2] = 0
+    run = URun(wl)
+    before = [run.flat_host(w) for w in range(W)]
+    ddp = run.ddp
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_set_local_used(run.r, used)
+    unused = {p for p in range(P) if not any(used[w][p] for w in range(W))}
+    ddp.ddp_mark_ready_many(run.r, [p for p in range(P - 1, -1, -1) if p not in unused])
+    ddp.ddp_finish(run.r, host_blocking=True)
+    check(run, used, before)
+    run.close()

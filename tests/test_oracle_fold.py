@@ -240,3 +240,26 @@ def test_reduce_scatter_shards_tile_the_bucket_and_are_exact_on_a_dyadic_grid():
     exact = ks.sum(axis=0) * 2.0 ** -10 / W
     for lo, hi, vals in rs:
         np.testing.assert_array_equal(vals.astype(np.float64), exact[lo:hi])
+
+
+def test_partially_used_parameter_mean_is_half_of_the_user_gradient():
+    """Two replicas, the parameter used on replica 0 only: replica 1's slice
+    is zero-filled, so the result is g0 / 2 exactly [L15 §4.2]."""
+    rng = np.random.default_rng(21)
+    g0 = rng.standard_normal(333).astype(np.float32)
+    out = _fold().reduce_f32([g0, np.zeros_like(g0)])
+    np.testing.assert_array_equal(out, g0 * np.float32(0.5))
+
+
+def test_three_accumulation_schedules_agree_on_a_dyadic_grid():
+    """Reducing every micro-batch, reducing the locally accumulated sum once,
+    or reducing twice and adding give the same result because the mean is
+    linear [L15 §4.1] (exact on a dyadic grid)."""
+    rng = np.random.default_rng(22)
+    W, n, micro = 4, 500, 4
+    mb = [[(rng.integers(-128, 129, n) * 2.0 ** -12).astype(np.float32) for _ in range(W)] for _ in range(micro)]
+    f = _fold()
+    each = sum(f.reduce_f32(m).astype(np.float64) for m in mb)
+    local = [sum(mb[k][w].astype(np.float64) for k in range(micro)).astype(np.float32) for w in range(W)]
+    once = f.reduce_f32(local).astype(np.float64)
+    np.testing.assert_array_equal(each, once)

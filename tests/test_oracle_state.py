@@ -122,3 +122,57 @@ def test_reset_and_rearm():
             m.mark_ready(0)       # still ready until the next prepare
         m.prepare_for_backward()
     assert m.launched == [0, 1, 2] * 3
+
+
+def test_no_sync_passes_launch_nothing_and_the_next_synced_pass_does():
+    """Inside no_sync the hooks are disabled; the next synchronized backward
+    launches every bucket as usual [L15 §4.1; PTD-notes §2.2.4]."""
+    plan = plan_buckets([4] * 6, REVERSE, cap=8, first_cap=8)
+    m = ReducerModel(plan.buckets, 6)
+    m.set_require_sync(False)
+    for _ in range(3):
+        m.prepare_for_backward()
+        for p in range(5, -1, -1):
+            assert m.mark_ready(p) == []
+        m.finish()
+    m.set_require_sync(True)
+    m.prepare_for_backward()
+    got = []
+    for p in range(5, -1, -1):
+        got += m.mark_ready(p)
+    assert got == [0, 1, 2]
+    m.finish()
+
+
+def test_globally_unused_parameters_are_ready_at_the_first_hook():
+    """A parameter no replica used is marked ready when the first gradient
+    arrives, so its bucket can launch without it [DDP-ch17 §17.33]."""
+    plan = plan_buckets([4] * 4, REVERSE, cap=8, first_cap=8)   # [[3,2],[1,0]]
+    m = ReducerModel(plan.buckets, 4, world=2, find_unused=True)
+    m.prepare_for_backward()
+    # parameter 2 unused everywhere, parameter 0 used on replica 1 only
+    m.set_local_used([[1, 0, 0, 1], [1, 1, 0, 1]])
+    assert m.globally_unused() == [2]
+    assert m.mark_ready(3) == [0]          # bucket 0 = {3, 2}: 2 was marked at this first hook
+    assert m.mark_ready(1) == []
+    assert m.mark_ready(0) == [1]
+    m.finish()
+    # the used table is cleared after the synchronized pass
+    assert m.used_mask() == [[1] * 4, [1] * 4]
+
+
+def test_used_tables_accumulate_through_no_sync_passes():
+    plan = plan_buckets([4] * 3, REVERSE, cap=100, first_cap=100)
+    m = ReducerModel(plan.buckets, 3, world=2, find_unused=True)
+    m.set_require_sync(False)
+    m.prepare_for_backward()
+    m.set_local_used([[1, 0, 0], [0, 0, 0]])
+    m.finish()
+    m.set_require_sync(True)
+    m.prepare_for_backward()
+    m.set_local_used([[0, 0, 0], [0, 1, 0]])
+    assert m.used_mask() == [[1, 0, 0], [0, 1, 0]]
+    assert m.globally_unused() == [2]
+    m.mark_ready(1)
+    with pytest.raises(ModelError):            # too late once the backward has started
+        m.set_local_used([[1, 1, 1], [1, 1, 1]])
