@@ -22,6 +22,8 @@ Parts:
                    O5  the same fold split over host threads (identical bits)
   ring.py          O4  literal ring reduce-scatter + all-gather simulation (tiny inputs)
   fold.py          O6  reduce-scatter only (ZeRO-1): replica c keeps chunk c of the mean
+  compress.py      O7  bf16 / fp16 compression hooks: cast, divide by W, fold with the sum
+                       rounded to the wire format at every hop, widen back to fp32
 
 Every function is pinned by tests under ``tests/`` (``-m "not gpu"``) against
 the pages' worked examples, closed forms, brute force and invariants.
@@ -30,6 +32,7 @@ from .plan import Plan, plan_buckets, REVERSE, GIVEN, FWD_THEN_REVERSE  # noqa: 
 from .reducer_model import ReducerModel, ModelError, comm_timeline  # noqa: F401
 from .ring import ring_allreduce, ring_reduce_scatter  # noqa: F401
 from . import fold  # noqa: F401
+from . import compress  # noqa: F401
 
 
 def build(verbose: bool = False) -> None:

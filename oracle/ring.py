@@ -19,9 +19,11 @@ reference for large buckets.
 """
 from __future__ import annotations
 
-from typing import List, Optional, Sequence
+from typing import Callable, List, Optional, Sequence
 
 import numpy as np
+
+Rounding = Callable[[np.ndarray], np.ndarray]
 
 
 def _chunks(n: int, W: int):
@@ -29,12 +31,19 @@ def _chunks(n: int, W: int):
     return [(min(c * q, n), min((c + 1) * q, n)) for c in range(W)]
 
 
-def ring_allreduce(grads: Sequence[np.ndarray], wgrad_bf16: Optional[Sequence[np.ndarray]] = None) -> List[np.ndarray]:
+def ring_allreduce(grads: Sequence[np.ndarray], wgrad_bf16: Optional[Sequence[np.ndarray]] = None,
+                   wire: Optional[Rounding] = None) -> List[np.ndarray]:
     """Returns every rank's buffer after the all-gather.
 
     grads: W float32 arrays (the fp32 gradients, or the main_grad values when
     wgrad_bf16 is given). wgrad_bf16: W uint16 arrays of bf16 bit patterns,
-    added in fp32 to grads before scaling."""
+    added in fp32 to grads before scaling.
+
+    wire: a compression hook's 16-bit format, given as its rounding (fp32
+    values in, the nearest wire values out, as fp32) [DDP-ch17 §17.9]. Each
+    rank then casts its bucket to the wire format and divides it by W
+    (rounded again), and every hop's sum is rounded to the wire format; the
+    buffers stay in the wire format through the all-gather."""
     W = len(grads)
     n = grads[0].size
     s = np.float32(1.0) / np.float32(W)
@@ -44,7 +53,11 @@ def ring_allreduce(grads: Sequence[np.ndarray], wgrad_bf16: Optional[Sequence[np
         if wgrad_bf16 is not None:
             wide = (np.asarray(wgrad_bf16[r], dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
             g = (g + wide).astype(np.float32)
-        bufs.append((g * s).astype(np.float32))
+        if wire is None:
+            bufs.append((g * s).astype(np.float32))
+        else:
+            with np.errstate(over="ignore", invalid="ignore"):
+                bufs.append(wire((wire(g) / np.float32(W)).astype(np.float32)))
     ch = _chunks(n, W)
 
     # reduce-scatter
@@ -55,7 +68,9 @@ def ring_allreduce(grads: Sequence[np.ndarray], wgrad_bf16: Optional[Sequence[np
             lo, hi = ch[c]
             sends.append(((r + 1) % W, lo, hi, bufs[r][lo:hi].copy()))
         for dst, lo, hi, data in sends:
-            bufs[dst][lo:hi] = (bufs[dst][lo:hi] + data).astype(np.float32)
+            with np.errstate(over="ignore", invalid="ignore"):
+                summed = (bufs[dst][lo:hi] + data).astype(np.float32)
+            bufs[dst][lo:hi] = summed if wire is None else wire(summed)
 
     # all-gather
     for step in range(W - 1):
