@@ -43,9 +43,13 @@ def host_cores() -> int:
         return os.cpu_count() or 1
 
 
+HOOKS = {"none": 0, "bf16": 1, "fp16": 2}          # DDP_HOOK_ALLREDUCE, _BF16_COMPRESS, _FP16_COMPRESS
+HOOK_FORMATS = {1: "bf16", 2: "fp16"}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("bucket_reduce.hip", "internal.h"):
+    for f in ("reduce_kernels.h", "internal.h", "bucket_reduce.hip", "bucket_bf16_hook.hip", "bucket_fp16_hook.hip"):
         with open(os.path.join(ROOT, "bucketed_gradient_all_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -151,13 +155,14 @@ class Session:
         return time.perf_counter() - t0
 
 
-def cpu_baseline(wl, session, target_s: float):
+def cpu_baseline(wl, session, target_s: float, hook: int = 0):
     """The oracle (threaded fold, as written) on the first buckets of the
-    same workload, inputs regenerated on the host; only the fold is timed."""
+    same workload, inputs regenerated on the host; only the fold is timed.
+    With a compression hook the oracle is the single-threaded numpy one."""
     import numpy as np
 
     import synth
-    from oracle import fold
+    from oracle import compress, fold
     from oracle.plan import plan_buckets
     from synth.workloads import IN_BF16_ACCUM_F32, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD
 
@@ -172,7 +177,7 @@ def cpu_baseline(wl, session, target_s: float):
         chosen.append(b)
         acc += nb
     sc = synth.scale_for(wl.dist, wl.sigma)
-    threads = max(1, min(host_cores(), 64))
+    threads = 1 if hook else max(1, min(host_cores(), 64))
 
     def gen_bucket(b):
         n = oplan.bucket_bytes[b] // 4
@@ -200,7 +205,10 @@ def cpu_baseline(wl, session, target_s: float):
         outs = []
         t = time.perf_counter()
         for xs, gs in data:
-            if wl.input_mode == IN_BF16_ACCUM_F32:
+            if hook:
+                outs.append(compress.compressed_reduce(HOOK_FORMATS[hook], xs,
+                                                       gs if wl.input_mode == IN_BF16_ACCUM_F32 else None))
+            elif wl.input_mode == IN_BF16_ACCUM_F32:
                 outs.append(fold.reduce_bf16acc(xs, gs, nthreads=nthreads))
             else:
                 outs.append(fold.reduce_f32(xs, nthreads=nthreads))
@@ -288,6 +296,8 @@ def main():
     ap.add_argument("--workload", default="resnet50",
                     help="tiny | resnet50 | bert_large | megatron_llama1b | sweep_w{W}_cap{MiB}")
     ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
+    ap.add_argument("--hook", default="none", choices=list(HOOKS),
+                    help="built-in communication hook: the fp32 mean, or bf16 / fp16 compression")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-ms", type=float, default=20.0,
@@ -340,10 +350,14 @@ def main():
     if args.collective == "reduce_scatter":
         wl.collective = wls.REDUCE_SCATTER
         wl.name += "_rs"
+    hook = HOOKS[args.hook]
+    if hook:
+        wl.name += f"_{args.hook}hook"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
     s = Session(wl)
     import bucketed_gradient_all_amd as ddp
+    ddp.ddp_register_builtin_hook(s.r, hook)
     bytes_per_step = wl.algorithmic_bytes()
 
     for _ in range(args.warmup):
@@ -371,7 +385,8 @@ def main():
     launches = len(ms)
     per_launch_bytes = sum(launch_bytes) / max(launches, 1)
     achieved = sum(launch_bytes) / kernel_s / 1e9 if kernel_s > 0 else 0.0
-    bus = sum(2 * (W - 1) / W * b for b in s.bucket_bytes) / step_s / 1e9
+    wire = 0.5 if hook else 1.0      # a compression hook sends 2-byte values instead of 4-byte ones
+    bus = sum(2 * (W - 1) / W * b * wire for b in s.bucket_bytes) / step_s / 1e9
 
     # one launch per bucket (each bucket's ready call separate): step time and
     # per-bucket kernel rates (median over steps)
@@ -411,7 +426,7 @@ def main():
         s.inputs.refill()
         s.step()
         torch.cuda.synchronize()
-        cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds)
+        cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds, hook)
 
     traffic = measured_traffic(wl.name)
     out = {
@@ -431,6 +446,7 @@ def main():
                    "buckets": s.plan.n_buckets, "cap_bytes": wl.cap_bytes, "first_cap_bytes": wl.first_cap_bytes,
                    "input_mode": MODE_NAMES[wl.input_mode], "bytes_per_step": bytes_per_step,
                    "collective": "reduce_scatter" if wl.collective == wls.REDUCE_SCATTER else "all_reduce",
+                   "hook": args.hook,
                    "parallelism": "1 GPU, W replicas in HBM"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "bus_bw_GBps": round(bus, 2),

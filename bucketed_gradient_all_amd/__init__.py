@@ -36,19 +36,40 @@ DDP_ORDER_FWD_THEN_REVERSE = 2
 DDP_ALL_REDUCE = 0
 DDP_REDUCE_SCATTER = 1
 
+DDP_HOOK_ALLREDUCE = 0
+DDP_HOOK_BF16_COMPRESS = 1
+DDP_HOOK_FP16_COMPRESS = 2
+
 DDP_IN_F32_COPY = 0
 DDP_IN_F32_VIEW = 1
 DDP_IN_BF16_ACCUM_F32 = 2
 
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                "-ffp-contract=off", "-fno-fast-math",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+# one object per source; the kernel families compile in parallel
+SOURCES = ["reducer.cpp", "bucket_reduce.hip", "bucket_bf16_hook.hip", "bucket_fp16_hook.hip"]
+HEADERS = ["internal.h", "reduce_kernels.h"]
 
 
 def build(verbose: bool = False) -> None:
     """Compile libddp.so in place with hipcc for gfx950."""
-    srcs = [os.path.join(CSRC, "reducer.cpp"), os.path.join(CSRC, "bucket_reduce.hip")]
-    cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-o", LIB_PATH + ".tmp", *srcs]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".", "_") + ".o")
+        cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj,
+               os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, cwd=HERE)))
+        objs.append(obj)
+    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB_PATH + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, cwd=HERE)
@@ -114,6 +135,7 @@ def lib():
             "ddp_get_timings": [P, P, P, P, I32, P],
             "ddp_set_require_sync": [P, I32],
             "ddp_set_local_used": [P, P],
+            "ddp_register_builtin_hook": [P, I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -289,6 +311,10 @@ def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> No
         return
     r._hook = HOOK_FN(lambda ctx, b: int(fn(b)))
     _check(lib().ddp_register_comm_hook(r.handle, r._hook, None))
+
+
+def ddp_register_builtin_hook(r: Reducer, hook: int) -> None:
+    _check(lib().ddp_register_builtin_hook(r.handle, int(hook)))
 
 
 def ddp_get_bucket(r: Reducer, bucket: int):

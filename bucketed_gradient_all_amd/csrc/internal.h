@@ -1,5 +1,6 @@
 // Internal types shared by the host reducer (reducer.cpp) and the bucket
-// reduction kernels (bucket_reduce.hip). Not part of the C ABI.
+// reduction kernels (reduce_kernels.h and the .hip files that instantiate
+// them). Not part of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -47,13 +48,29 @@ struct KernelTables {
     int32_t n_params;
 };
 
-// Enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on stream s:
-// all-reduce (the sum stored to every replica) or reduce-scatter (chunk c
-// stored to replica c only). Returns hipSuccess or the launch error.
-// With t.used set, a replica whose bit is clear contributes a zero-filled
-// slice (its source is not read) and a gradient no replica used is not
-// written at all.
-hipError_t launch_bucket_reduce(int mode, int W, bool reduce_scatter, float scale, const KernelTables &t,
-                                int32_t tile_begin, int32_t n_tiles, hipStream_t s);
+// Scaling of one replica's term. The mean multiplies by s = fp32(1/W); the
+// compression hooks divide by w = W, or multiply by s when divide is 0 (W a
+// power of two, where both give the same quotient).
+struct Scale {
+    float s;
+    float w;
+    int32_t divide;
+};
+
+// Each enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on
+// stream s: all-reduce (the sum stored to every replica) or reduce-scatter
+// (chunk c stored to replica c only), and returns hipSuccess or the launch
+// error. With t.used set, a replica whose bit is clear contributes a
+// zero-filled slice (its source is not read) and a gradient no replica used
+// is not written at all.
+//   launch_mean:       the fp32 mean (no communication hook)
+//   launch_bf16_hook:  through the bf16 compression hook
+//   launch_fp16_hook:  through the fp16 compression hook
+hipError_t launch_mean(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
+                       int32_t tile_begin, int32_t n_tiles, hipStream_t s);
+hipError_t launch_bf16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
+                            int32_t tile_begin, int32_t n_tiles, hipStream_t s);
+hipError_t launch_fp16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
+                            int32_t tile_begin, int32_t n_tiles, hipStream_t s);
 
 }  // namespace ddp

@@ -1,0 +1,475 @@
+// Device templates of the bucket reduction, shared by the translation units
+// that instantiate them (bucket_reduce.hip: the fp32 mean; bucket_bf16_hook.hip
+// and bucket_fp16_hook.hip: the compression hooks). Not part of the C ABI.
+//
+// One launch reduces a range of tiles over W replicas resident in HBM: for
+// every element it reads the W replicas' values, forms each replica's term,
+// sums the terms in the ring all-reduce's order for the element's chunk and
+// writes the sum to all W flat buffers (or to the chunk owner's only). This
+// fuses three steps of the pages' design into a single pass over HBM: the
+// copy of each gradient into its bucket with its scaling [DDP-ch17 §17.9,
+// §17.12], the reduce-scatter half of the ring and its all-gather half
+// [DDP-ch17 §17.4]; in bf16 mode the accumulation of the bf16 weight
+// gradient into the fp32 main_grad is fused in as well [MegatronDDP §1].
+//
+// Terms and sums per hook:
+//   mean:            t = y * fp32(1/W);            acc = acc + t
+//   bf16/fp16 hook:  t = R(R(y) / W);              acc = R(acc + t)
+// with y the replica's gradient (or main_grad + wgrad), R the round-to-
+// nearest-even conversion to the 16-bit wire format (kept widened in fp32
+// registers) and every operation rounded on its own (no contraction), so the
+// results equal the CPU oracle bit for bit. The compression hooks cast, then
+// divide by W, and round each hop's sum to the wire format [DDP-ch17 §17.9];
+// the decompressed result is the widened wire value.
+//
+// It is a streaming reduction (a few ALU operations per element against 8 or
+// 10 bytes of HBM traffic per element and replica), far below the fp32 ridge
+// point, so it runs on the vector ALUs; the design aims only at HBM:
+//   * the host cuts each bucket into segments that lie inside one gradient
+//     tensor and one ring chunk, so a workgroup has one source tensor and one
+//     fold order (wave-uniform addresses in scalar registers, no per-lane
+//     branching on the chunk);
+//   * the fold order is fixed at compile time by loading replica (c + k) mod W
+//     into register slot k, so the order is a plain slot-0..W-1 sum;
+//   * 16-byte vector loads and stores (8-byte for bf16), every load of a
+//     thread issued before the first add, non-temporal hints on the streamed
+//     data so it does not evict other lines from L2 / MALL.
+// The reduce-scatter variant (ZeRO-1 [MegatronDDP §3]) folds the same way but
+// stores chunk c only to replica c's flat buffer. With unused-parameter
+// detection, a replica that did not use a gradient contributes a zero-filled
+// slice (its source is not read), and a gradient no replica used is left
+// untouched [DDP-ch17 §17.33].
+#pragma once
+
+#include "internal.h"
+
+#include <hip/hip_runtime.h>
+
+namespace ddp {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+enum { MODE_COPY = 0, MODE_VIEW = 1, MODE_BF16 = 2 };
+enum { HOOK_MEAN = 0, HOOK_BF16 = 1, HOOK_FP16 = 2 };
+
+__device__ __forceinline__ float widen(unsigned short b)
+{
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// R: round to the wire format, returned widened. Both use gfx950's
+// conversion instructions (v_cvt_pk_bf16_f32, v_cvt_f16_f32) under the
+// default mode: round to nearest even, overflow to inf, subnormals kept
+// (the kernels run with fp32 and fp16 denormals enabled), NaN stays NaN.
+// The empty asm pins v as an fp32 register value: without it the compiler
+// merges the fp32 multiply or add that produced v with the conversion into
+// one mixed-precision FMA (v_fma_mix*_f16 with a +0 addend), which rounds
+// once instead of twice and turns a -0 product into +0.
+template <int HOOK>
+__device__ __forceinline__ float wire(float v)
+{
+    if (HOOK == HOOK_BF16) return static_cast<float>(static_cast<__bf16>(v));
+    if (HOOK == HOOK_FP16) {
+        asm volatile("" : "+v"(v));
+        return static_cast<float>(static_cast<_Float16>(v));
+    }
+    return v;
+}
+
+// Every buffer the kernels touch is device (global) memory; saying so lets
+// the compiler emit global_* rather than flat_* memory instructions, which
+// only count against the vector-memory counter.
+#define GLOBAL __attribute__((address_space(1)))
+
+__device__ __forceinline__ f32x4 ld4(const float *p)
+{
+    return __builtin_nontemporal_load((const GLOBAL f32x4 *)(p));
+}
+
+__device__ __forceinline__ u16x4 ld4h(const unsigned short *p)
+{
+    return __builtin_nontemporal_load((const GLOBAL u16x4 *)(p));
+}
+
+__device__ __forceinline__ void st4(float *p, f32x4 v)
+{
+    __builtin_nontemporal_store(v, (GLOBAL f32x4 *)(p));
+}
+
+__device__ __forceinline__ float ld1(const float *p)
+{
+    return *(const GLOBAL float *)(p);
+}
+
+__device__ __forceinline__ unsigned short ld1h(const unsigned short *p)
+{
+    return *(const GLOBAL unsigned short *)(p);
+}
+
+__device__ __forceinline__ void st1(float *p, float v)
+{
+    *(GLOBAL float *)(p) = v;
+}
+
+// How a compression hook divides by W: DIV_MUL multiplies by s = fp32(1/W)
+// (W a power of two: the same quotient as a division), DIV_TRUE divides,
+// DIV_RUNTIME reads the choice from the Scale (W only known at run time).
+enum { DIV_MUL = 0, DIV_TRUE = 1, DIV_RUNTIME = 2 };
+
+constexpr int div_for(int W)
+{
+    return (W & (W - 1)) == 0 ? DIV_MUL : DIV_TRUE;
+}
+
+// One replica's term. y = x, or main + wgrad in bf16 mode; the mean scales
+// by s = fp32(1/W); a compression hook casts, divides by W and casts.
+template <int MODE, int HOOK, int DIV>
+__device__ __forceinline__ float term1(float x, unsigned short g, const Scale &sc)
+{
+    const float y = MODE == MODE_BF16 ? __fadd_rn(x, widen(g)) : x;
+    if (HOOK == HOOK_MEAN) return __fmul_rn(y, sc.s);
+    const float h = wire<HOOK>(y);
+    const bool divide = DIV == DIV_TRUE || (DIV == DIV_RUNTIME && sc.divide);
+    return wire<HOOK>(divide ? __fdiv_rn(h, sc.w) : __fmul_rn(h, sc.s));
+}
+
+template <int HOOK>
+__device__ __forceinline__ float add1(float a, float b)
+{
+    return wire<HOOK>(__fadd_rn(a, b));
+}
+
+template <int MODE, int HOOK, int DIV>
+__device__ __forceinline__ f32x4 term4(f32x4 x, u16x4 g, const Scale &sc)
+{
+    return f32x4{term1<MODE, HOOK, DIV>(x.x, g.x, sc), term1<MODE, HOOK, DIV>(x.y, g.y, sc),
+                 term1<MODE, HOOK, DIV>(x.z, g.z, sc), term1<MODE, HOOK, DIV>(x.w, g.w, sc)};
+}
+
+template <int HOOK>
+__device__ __forceinline__ f32x4 add4(f32x4 a, f32x4 b)
+{
+    return f32x4{add1<HOOK>(a.x, b.x), add1<HOOK>(a.y, b.y), add1<HOOK>(a.z, b.z), add1<HOOK>(a.w, b.w)};
+}
+
+__device__ __forceinline__ int slot_replica(int chunk, int k, int W)
+{
+    int r = chunk + k;
+    return r >= W ? r - W : r;
+}
+
+// Source of replica r for a segment: the gradient tensor (COPY, bf16 wgrad)
+// or the flat buffer itself (VIEW).
+template <int MODE>
+__device__ __forceinline__ const float *src_f32(const KernelTables &T, const DeviceSeg &sg, int r)
+{
+    if (MODE == MODE_COPY) return static_cast<const float *>(T.grads[int64_t(r) * T.n_params + sg.param]) + sg.src;
+    return T.flat[r] + sg.flat;   // VIEW input and bf16-mode main_grad live in the flat buffer
+}
+
+__device__ __forceinline__ const unsigned short *src_bf16(const KernelTables &T, const DeviceSeg &sg, int r)
+{
+    return static_cast<const unsigned short *>(T.grads[int64_t(r) * T.n_params + sg.param]) + sg.src;
+}
+
+__device__ __forceinline__ uint64_t used_mask(const KernelTables &T, const DeviceSeg &sg)
+{
+    return T.used ? T.used[sg.param] : ~uint64_t(0);
+}
+
+// One element, any W: used for unaligned heads and tails and for segments
+// whose pointers do not allow 16-byte vectors.
+template <int MODE, int HOOK>
+__device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t e, const Scale &sc, int W, bool rs)
+{
+    const uint64_t m = used_mask(T, sg);
+    float acc = 0.0f;
+    for (int k = 0; k < W; ++k) {
+        const int r = slot_replica(sg.chunk, k, W);
+        float t = 0.0f;
+        if ((m >> r) & 1) {
+            float x = ld1(src_f32<MODE>(T, sg, r) + e);
+            unsigned short g = MODE == MODE_BF16 ? ld1h(src_bf16(T, sg, r) + e) : 0;
+            t = term1<MODE, HOOK, DIV_RUNTIME>(x, g, sc);
+        }
+        acc = k == 0 ? t : add1<HOOK>(acc, t);
+    }
+    if (rs) {
+        st1(T.flat[sg.chunk] + sg.flat + e, acc);
+        return;
+    }
+    for (int w = 0; w < W; ++w) st1(T.flat[w] + sg.flat + e, acc);
+}
+
+// Heads, tails and scalar-only segments of a tile.
+template <int MODE, int HOOK>
+__device__ __forceinline__ void scalar_parts(const KernelTables &T, const DeviceSeg &sg, int64_t tin, int64_t tile,
+                                             const Scale &sc, int W, bool rs)
+{
+    const int tid = threadIdx.x;
+    if (sg.head >= 0) {
+        if (tin != 0) return;
+        const int64_t body = (sg.len - sg.head) / 4 * 4;
+        const int64_t tail = sg.len - sg.head - body;
+        if (tid < sg.head) fold_scalar<MODE, HOOK>(T, sg, tid, sc, W, rs);
+        if (tid >= 64 && tid < 64 + tail) fold_scalar<MODE, HOOK>(T, sg, sg.head + body + (tid - 64), sc, W, rs);
+        return;
+    }
+    const int64_t base = tin * tile;
+    for (int64_t j = tid; j < tile; j += kThreads) {
+        const int64_t e = base + j;
+        if (e < sg.len) fold_scalar<MODE, HOOK>(T, sg, e, sc, W, rs);
+    }
+}
+
+// One element with W known at compile time, from hoisted pointers; the sum
+// goes to the NOUT destinations (all W replicas, or the chunk's owner).
+template <int W, int NOUT, int MODE, int HOOK, bool USED>
+__device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
+                                                  float *const (&ds)[NOUT], const bool (&on)[W], int64_t e,
+                                                  const Scale &sc)
+{
+    float t[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        if (!USED || on[k])
+            t[k] = term1<MODE, HOOK, div_for(W)>(ld1(xs[k] + e), MODE == MODE_BF16 ? ld1h(gs[k] + e) : 0, sc);
+        else
+            t[k] = 0.0f;
+    }
+    float acc = t[0];
+#pragma unroll
+    for (int k = 1; k < W; ++k) acc = add1<HOOK>(acc, t[k]);
+#pragma unroll
+    for (int w = 0; w < NOUT; ++w) st1(ds[w] + e, acc);
+}
+
+// The 16-byte-vector part of one tile: U groups of 4 elements per thread.
+// CHECK = false: the whole tile lies inside the segment body (the common
+// case), so the block is straight-line code: all W*U loads, then the folds,
+// then all stores. CHECK = true: the segment's last tile, with per-lane
+// bounds; out-of-range lanes load the segment's first vector (in bounds, value
+// unused) and skip their stores.
+template <int W, int NOUT, int MODE, int HOOK, bool CHECK, bool USED>
+__device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
+                                            float *const (&ds)[NOUT], const bool (&on)[W], const DeviceSeg &sg,
+                                            int64_t tin, const Scale &sc)
+{
+    constexpr int U = unroll_for(W);
+    constexpr int64_t TILE = tile_elems(W);
+    const int tid = int(threadIdx.x);
+    int64_t e[U], el[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        e[u] = sg.head + tin * TILE + int64_t(u * kThreads + tid) * 4;
+        ok[u] = !CHECK || e[u] + 4 <= sg.len;
+        el[u] = ok[u] ? e[u] : int64_t(sg.head);
+    }
+    f32x4 v[U][W];
+    u16x4 g[U][W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        if (USED && !on[k]) {
+            // a replica that did not use this gradient: zero-filled slice, not read
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                v[u][k] = f32x4{0, 0, 0, 0};
+                g[u][k] = u16x4{0, 0, 0, 0};
+            }
+            continue;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v[u][k] = ld4(xs[k] + el[u]);
+            g[u][k] = MODE == MODE_BF16 ? ld4h(gs[k] + el[u]) : u16x4{0, 0, 0, 0};
+        }
+    }
+    f32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        acc[u] = (USED && !on[0]) ? f32x4{0, 0, 0, 0} : term4<MODE, HOOK, div_for(W)>(v[u][0], g[u][0], sc);
+#pragma unroll
+        for (int k = 1; k < W; ++k)
+            acc[u] = add4<HOOK>(acc[u], (USED && !on[k]) ? f32x4{0, 0, 0, 0}
+                                                         : term4<MODE, HOOK, div_for(W)>(v[u][k], g[u][k], sc));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (ok[u]) {
+#pragma unroll
+            for (int w = 0; w < NOUT; ++w) st4(ds[w] + e[u], acc[u]);
+        }
+}
+
+// W known at compile time: fully unrolled over replicas and vector groups.
+// All table reads (segment, source and destination pointers) happen before
+// the first store, so they stay in scalar registers; a table read after a
+// store would have to go through the vector memory path and wait for every
+// outstanding store.
+template <int W, int MODE, int HOOK, bool RS, bool USED>
+__global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, Scale sc)
+{
+    constexpr int NOUT = RS ? 1 : W;
+    constexpr int64_t TILE = tile_elems(W);
+    const int32_t tile = tile_begin + int32_t(blockIdx.x);
+    const DeviceSeg sg = T.segs[T.tile_seg[tile]];
+    const int64_t tin = int64_t(tile - sg.tile0);
+
+    // slot k holds replica (chunk + k) mod W, so the fold is slot 0, 1, ..., W-1
+    const float *xs[W];
+    const unsigned short *gs[W];
+    float *ds[NOUT];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const int r = slot_replica(sg.chunk, k, W);
+        xs[k] = src_f32<MODE>(T, sg, r);
+        gs[k] = MODE == MODE_BF16 ? src_bf16(T, sg, r) : nullptr;
+    }
+    if (RS) {
+        ds[0] = T.flat[sg.chunk] + sg.flat;   // chunk c belongs to replica c
+    } else {
+#pragma unroll
+        for (int w = 0; w < NOUT; ++w) ds[w] = T.flat[w] + sg.flat;
+    }
+
+    bool on[W];
+    if (USED) {
+        const uint64_t m = T.used[sg.param];
+        if (m == 0) return;   // no replica used this gradient: leave it untouched
+#pragma unroll
+        for (int k = 0; k < W; ++k) on[k] = (m >> slot_replica(sg.chunk, k, W)) & 1;
+    } else {
+#pragma unroll
+        for (int k = 0; k < W; ++k) on[k] = true;
+    }
+
+    const int tid = int(threadIdx.x);
+    if (sg.head >= 0) {
+        if (sg.head + (tin + 1) * TILE <= sg.len)
+            vector_tile<W, NOUT, MODE, HOOK, false, USED>(xs, gs, ds, on, sg, tin, sc);
+        else if (sg.len - sg.head >= 4)
+            vector_tile<W, NOUT, MODE, HOOK, true, USED>(xs, gs, ds, on, sg, tin, sc);
+        if (tin == 0) {
+            const int64_t body = (sg.len - sg.head) / 4 * 4;
+            const int64_t tail = sg.len - sg.head - body;
+            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED>(xs, gs, ds, on, tid, sc);
+            if (tid >= 64 && tid < 64 + tail)
+                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED>(xs, gs, ds, on, sg.head + body + (tid - 64), sc);
+        }
+        return;
+    }
+    for (int64_t j = tid; j < TILE; j += kThreads) {
+        const int64_t e = tin * TILE + j;
+        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED>(xs, gs, ds, on, e, sc);
+    }
+}
+
+// Any W: replicas are taken eight at a time, in fold order.
+template <int MODE, int HOOK>
+__global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32_t tile_begin, Scale sc, int W,
+                                                           int rs)
+{
+    const int64_t TILE = tile_elems(W);
+    const int32_t tile = tile_begin + int32_t(blockIdx.x);
+    const DeviceSeg sg = T.segs[T.tile_seg[tile]];
+    const int64_t tin = int64_t(tile - sg.tile0);
+    const uint64_t m = used_mask(T, sg);
+    if (m == 0) return;   // no replica used this gradient: leave it untouched
+
+    if (sg.head >= 0) {
+        for (int64_t e = sg.head + tin * TILE + int64_t(threadIdx.x) * 4; e < sg.head + (tin + 1) * TILE;
+             e += int64_t(kThreads) * 4) {
+            if (e + 4 > sg.len) break;
+            f32x4 acc = f32x4{0, 0, 0, 0};
+            for (int k0 = 0; k0 < W; k0 += 8) {
+                f32x4 v[8];
+                u16x4 g[8];
+                bool on[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    on[j] = false;
+                    if (k0 + j < W) {
+                        const int r = slot_replica(sg.chunk, k0 + j, W);
+                        on[j] = (m >> r) & 1;
+                        if (on[j]) {
+                            v[j] = ld4(src_f32<MODE>(T, sg, r) + e);
+                            g[j] = MODE == MODE_BF16 ? ld4h(src_bf16(T, sg, r) + e) : u16x4{0, 0, 0, 0};
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (k0 + j < W) {
+                        const f32x4 t = on[j] ? term4<MODE, HOOK, DIV_RUNTIME>(v[j], g[j], sc) : f32x4{0, 0, 0, 0};
+                        acc = (k0 + j == 0) ? t : add4<HOOK>(acc, t);
+                    }
+                }
+            }
+            if (rs) {
+                st4(T.flat[sg.chunk] + sg.flat + e, acc);
+            } else {
+                for (int w = 0; w < W; ++w) st4(T.flat[w] + sg.flat + e, acc);
+            }
+        }
+    }
+    scalar_parts<MODE, HOOK>(T, sg, tin, TILE, sc, W, rs != 0);
+}
+
+template <int W, int MODE, int HOOK>
+hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc, bool rs,
+                        hipStream_t st)
+{
+    const dim3 g(n_tiles), b(kThreads);
+    if (t.used) {
+        if (rs)
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true>), g, b, 0, st, t, tile_begin, sc);
+        else
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, true>), g, b, 0, st, t, tile_begin, sc);
+    } else {
+        if (rs)
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, false>), g, b, 0, st, t, tile_begin, sc);
+        else
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, false>), g, b, 0, st, t, tile_begin, sc);
+    }
+    return hipGetLastError();
+}
+
+template <int MODE, int HOOK>
+hipError_t dispatch_w(int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc,
+                      hipStream_t st)
+{
+    switch (W) {
+    case 1: return launch_fixed<1, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 2: return launch_fixed<2, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 3: return launch_fixed<3, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 4: return launch_fixed<4, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 5: return launch_fixed<5, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 6: return launch_fixed<6, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 7: return launch_fixed<7, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 8: return launch_fixed<8, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 16: return launch_fixed<16, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 32: return launch_fixed<32, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    default:
+        hipLaunchKernelGGL((reduce_generic<MODE, HOOK>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, sc, W,
+                           rs ? 1 : 0);
+        return hipGetLastError();
+    }
+}
+
+template <int HOOK>
+hipError_t dispatch_mode(int mode, int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles,
+                         const Scale &sc, hipStream_t st)
+{
+    switch (mode) {
+    case MODE_COPY: return dispatch_w<MODE_COPY, HOOK>(W, rs, t, tile_begin, n_tiles, sc, st);
+    case MODE_VIEW: return dispatch_w<MODE_VIEW, HOOK>(W, rs, t, tile_begin, n_tiles, sc, st);
+    case MODE_BF16: return dispatch_w<MODE_BF16, HOOK>(W, rs, t, tile_begin, n_tiles, sc, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+}  // namespace ddp

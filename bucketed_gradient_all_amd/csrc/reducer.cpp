@@ -211,7 +211,8 @@ Layout layout_of(const PlanView &pv)
 struct ddp_reducer {
     PlanView pv;
     bool device = false;
-    float scale = 1.0f;
+    ddp::Scale scale{1.0f, 1.0f, 0};
+    int32_t builtin_hook = DDP_HOOK_ALLREDUCE;   // kernel family of every launch
     KernelTables tables{};
     hipStream_t compute = nullptr, comm = nullptr;
     hipEvent_t ev_ready = nullptr, ev_done = nullptr;
@@ -297,7 +298,17 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
     }
     const int32_t tile0 = r->pv.tile_begin[b0];
     const int32_t tiles = r->pv.tile_begin[b1 - 1] + r->pv.tile_count[b1 - 1] - tile0;
-    e = ddp::launch_bucket_reduce(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+    switch (r->builtin_hook) {
+    case DDP_HOOK_BF16_COMPRESS:
+        e = ddp::launch_bf16_hook(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+        break;
+    case DDP_HOOK_FP16_COMPRESS:
+        e = ddp::launch_fp16_hook(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+        break;
+    default:
+        e = ddp::launch_mean(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+        break;
+    }
     if (e != hipSuccess) return hip_fail("bucket reduce launch", e);
     if (r->timing) {
         if ((e = hipEventRecord(r->t1[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
@@ -496,7 +507,9 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         return rc;
     }
     PlanView &pv = r->pv;
-    r->scale = 1.0f / float(pv.W);
+    r->scale.s = 1.0f / float(pv.W);
+    r->scale.w = float(pv.W);
+    r->scale.divide = (pv.W & (pv.W - 1)) != 0;   // W not a power of two
     r->device = desc->flat != nullptr;
     r->compute = static_cast<hipStream_t>(desc->compute_stream);
     r->comm = static_cast<hipStream_t>(desc->comm_stream);
@@ -729,6 +742,17 @@ int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     r->hook = fn;
     r->hook_ctx = ctx;
+    return DDP_OK;
+}
+
+int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (hook != DDP_HOOK_ALLREDUCE && hook != DDP_HOOK_BF16_COMPRESS && hook != DDP_HOOK_FP16_COMPRESS)
+        return fail(DDP_ERR_INVALID, "unknown built-in hook " + std::to_string(hook));
+    if (r->in_iteration())
+        return fail(DDP_ERR_UNFINISHED, "cannot change the hook while a backward is in flight");
+    r->builtin_hook = hook;
     return DDP_OK;
 }
 

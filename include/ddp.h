@@ -236,6 +236,28 @@ int ddp_set_local_used(ddp_reducer *r, const uint8_t *used);
 typedef int (*ddp_comm_hook_fn)(void *ctx, int32_t bucket);
 int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx);
 
+/* Built-in communication hooks [DDP-ch17 §17.9]: the arithmetic every
+ * bucket reduction of this reducer uses (the reducer's own launches and
+ * ddp_bucket_reduce, also from a callback hook).
+ *  DDP_HOOK_ALLREDUCE: the default; each replica's gradient is scaled by
+ *    fp32(1/W) and the terms are summed in fp32.
+ *  DDP_HOOK_BF16_COMPRESS / DDP_HOOK_FP16_COMPRESS: each replica's bucket
+ *    (in bf16 mode: main_grad + wgrad, summed in fp32) is cast to the 16-bit
+ *    wire format (round to nearest even) and divided by W in fp32, rounded to
+ *    the wire format again; every hop of the ring sum is an fp32 add rounded
+ *    to the wire format; the result is widened into the fp32 buckets. These
+ *    halve the bytes a collective would send and lose precision; fp16 turns a
+ *    gradient beyond its range (|x| >= 65520) into inf.
+ * The flat buffers stay fp32 in HBM, so the single-GPU pass moves the same
+ * HBM bytes under every hook. Errors: DDP_ERR_INVALID for an unknown hook;
+ * DDP_ERR_UNFINISHED while a backward is in flight. */
+enum {
+    DDP_HOOK_ALLREDUCE = 0,
+    DDP_HOOK_BF16_COMPRESS = 1,
+    DDP_HOOK_FP16_COMPRESS = 2
+};
+int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
+
 /* Plan introspection (bucket sizes and members, [DDP-ch17 §17.39]). */
 int ddp_get_bucket(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t *flat_offset_bytes,
                    int32_t *n_params);

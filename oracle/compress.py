@@ -117,3 +117,25 @@ def compressed_reduce_scatter(fmt: str, x: Sequence[np.ndarray], wgrad: Optional
     Returns [(lo, hi, values)] per replica."""
     full = compressed_reduce(fmt, x, wgrad)
     return [(lo, hi, full[lo:hi]) for lo, hi in _chunks(full.size, len(x))]
+
+
+def compressed_reduce_at(fmt: str, n: int, elems: np.ndarray, vals: np.ndarray,
+                         wg_vals: Optional[np.ndarray] = None) -> np.ndarray:
+    """The hook's result at chosen elements of a bucket of n elements.
+    elems: bucket element indices [m]; vals: the replicas' values there [m, W]
+    (main_grad values when wg_vals, bf16 patterns [m, W], is given). Same
+    arithmetic as compressed_reduce, one element at a time along the rows."""
+    elems = np.asarray(elems, dtype=np.int64)
+    vals = np.asarray(vals, dtype=np.float32)
+    m, W = vals.shape
+    cols = [vals[:, w] for w in range(W)]
+    wg = None if wg_vals is None else [np.asarray(wg_vals)[:, w] for w in range(W)]
+    d = np.stack(compressed_terms(fmt, cols, wg), axis=1) if m else np.zeros((0, W), np.float32)
+    q = -(-n // W)
+    c = elems // q
+    rows = np.arange(m)
+    acc = d[rows, c]
+    for k in range(1, W):
+        with np.errstate(over="ignore", invalid="ignore"):
+            acc = round_to(fmt, (acc + d[rows, (c + k) % W]).astype(np.float32))
+    return acc

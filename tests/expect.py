@@ -12,7 +12,7 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 import synth
-from oracle import fold
+from oracle import compress, fold
 from oracle.plan import plan_buckets
 from synth.workloads import (IN_BF16_ACCUM_F32, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD, Workload)
 
@@ -54,19 +54,25 @@ def bucket_inputs(wl: Workload, plan, b: int, seed: int, used=None):
     return xs, gs
 
 
-def expected_bucket(wl: Workload, plan, b: int, seed: int, nthreads: int = 0, used=None) -> np.ndarray:
+HOOK_FORMATS = {1: compress.BF16, 2: compress.FP16}   # DDP_HOOK_BF16_COMPRESS, DDP_HOOK_FP16_COMPRESS
+
+
+def expected_bucket(wl: Workload, plan, b: int, seed: int, nthreads: int = 0, used=None, hook: int = 0) -> np.ndarray:
     xs, gs = bucket_inputs(wl, plan, b, seed, used)
+    if hook:
+        return compress.compressed_reduce(HOOK_FORMATS[hook], xs,
+                                          gs if wl.input_mode == IN_BF16_ACCUM_F32 else None)
     if wl.input_mode == IN_BF16_ACCUM_F32:
         return fold.reduce_bf16acc(xs, gs, nthreads=nthreads)
     return fold.reduce_f32(xs, nthreads=nthreads)
 
 
-def expected_flat(wl: Workload, plan, seed: int, nthreads: int = 0, used=None) -> np.ndarray:
+def expected_flat(wl: Workload, plan, seed: int, nthreads: int = 0, used=None, hook: int = 0) -> np.ndarray:
     total = sum(plan.bucket_bytes) // 4
     out = np.empty(total, np.float32)
     for b in range(plan.n_buckets):
         o = plan.bucket_offset[b] // 4
-        out[o:o + plan.bucket_bytes[b] // 4] = expected_bucket(wl, plan, b, seed, nthreads, used)
+        out[o:o + plan.bucket_bytes[b] // 4] = expected_bucket(wl, plan, b, seed, nthreads, used, hook)
     return out
 
 
@@ -103,7 +109,8 @@ def sample_positions(wl: Workload, plan, per_param: int, rng: np.random.Generato
     return out
 
 
-def expected_at(wl: Workload, plan, positions: List[Tuple[int, int]], seed: int) -> Tuple[np.ndarray, np.ndarray]:
+def expected_at(wl: Workload, plan, positions: List[Tuple[int, int]], seed: int,
+                hook: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Flat element indices of `positions` and the oracle's value there."""
     sc = _scale(wl)
     W = wl.world
@@ -121,11 +128,12 @@ def expected_at(wl: Workload, plan, positions: List[Tuple[int, int]], seed: int)
                            for w in range(W)], axis=1)
             gv = np.stack([synth.host_gather_bf16(synth.key(seed, STREAM_WGRAD, w, p), wl.dist, sc, idx)
                            for w in range(W)], axis=1)
-            v = fold.reduce_at_bf16acc(n, e, mv, gv)
+            v = (compress.compressed_reduce_at(HOOK_FORMATS[hook], n, e, mv, gv) if hook
+                 else fold.reduce_at_bf16acc(n, e, mv, gv))
         else:
             xv = np.stack([synth.host_gather_f32(synth.key(seed, STREAM_GRAD, w, p), wl.dist, sc, idx)
                            for w in range(W)], axis=1)
-            v = fold.reduce_at_f32(n, e, xv)
+            v = compress.compressed_reduce_at(HOOK_FORMATS[hook], n, e, xv) if hook else fold.reduce_at_f32(n, e, xv)
         flat_idx.append(plan.bucket_offset[b] // 4 + e)
         vals.append(v)
     return np.concatenate(flat_idx), np.concatenate(vals)

@@ -370,3 +370,23 @@ def test_local_used_errors():
     assert e.value.code == ddp.DDP_ERR_INVALID
     with pytest.raises(ddp.DDPError):                   # more than 64 replicas
         ddp.ddp_reducer_create(ddp.Desc(65, [4], [0], [0], 1, find_unused=True))
+
+
+def test_builtin_hook_rules():
+    r, plan, log = host_reducer([4, 4, 4, 4], 8, 8)
+    for bad in (-1, 3, 99):
+        with pytest.raises(ddp.DDPError) as e:
+            ddp.ddp_register_builtin_hook(r, bad)
+        assert e.value.code == ddp.DDP_ERR_INVALID
+    for hook in (ddp.DDP_HOOK_BF16_COMPRESS, ddp.DDP_HOOK_FP16_COMPRESS, ddp.DDP_HOOK_ALLREDUCE):
+        ddp.ddp_register_builtin_hook(r, hook)
+    ddp.ddp_prepare_for_backward(r)
+    ddp.ddp_mark_ready(r, 3)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_register_builtin_hook(r, ddp.DDP_HOOK_BF16_COMPRESS)
+    assert e.value.code == ddp.DDP_ERR_UNFINISHED
+    for p in (2, 1, 0):
+        ddp.ddp_mark_ready(r, p)
+    ddp.ddp_finish(r)
+    ddp.ddp_register_builtin_hook(r, ddp.DDP_HOOK_BF16_COMPRESS)   # between iterations: allowed
+    ddp.ddp_reducer_destroy(r)

@@ -248,3 +248,17 @@ def test_bf16_division_and_reciprocal_agree_on_every_wire_value():
     for W in range(1, 65):
         div, mul = _div_and_mul(BF16, h, W)
         assert np.array_equal(div.view(np.uint32), mul.view(np.uint32)), W
+
+
+@pytest.mark.parametrize("fmt", [BF16, FP16])
+def test_sampled_elements_match_the_whole_bucket(fmt):
+    r = np.random.default_rng(11)
+    for W, n in ((1, 5), (3, 100), (8, 1001), (12, 37)):
+        xs = [r.normal(0, 1, n).astype(np.float32) for _ in range(W)]
+        wg = [C.bf16_bits(r.normal(0, 1, n).astype(np.float32)) for _ in range(W)]
+        for g in (None, wg):
+            full = C.compressed_reduce(fmt, xs, g)
+            e = r.permutation(n)[:min(n, 40)]
+            vals = np.stack([x[e] for x in xs], axis=1)
+            gv = None if g is None else np.stack([x[e] for x in g], axis=1)
+            assert np.array_equal(C.compressed_reduce_at(fmt, n, e, vals, gv), full[e])
