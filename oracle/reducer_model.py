@@ -31,6 +31,13 @@ Skipping synchronization and unused parameters:
   * the used tables keep accumulating through no_sync passes until the next
     synchronized one [PTD-notes §2.2.4].
 
+Bucket groups [MegatronDDP §3]: consecutive buckets whose collectives are
+issued together, as one coalesced call, so that a group pays one launch
+instead of one per bucket. Readings: a group is issued once every bucket in
+it is ready and every earlier group was issued (groups keep the strict
+order); by default each bucket is its own group; the grouping may change
+only between iterations.
+
 Reading: finishing an iteration whose buckets have not all launched is an
 error that lists, in ascending order, the parameters not marked ready.
 
@@ -71,6 +78,7 @@ class ReducerModel:
         if any(b < 0 for b in self.bucket_of):
             raise ModelError(ERR_INVALID)
         self.launched: List[int] = []      # every launch since construction
+        self.group_first = list(range(len(self.buckets)))   # each bucket its own group
         self.require_sync = True
         self.window_used = None            # [W][P] OR of used tables since the last synchronized pass
         self._reset()
@@ -86,6 +94,35 @@ class ReducerModel:
 
     def _unready(self) -> List[int]:
         return [p for p in range(self.P) if not self.ready[p]]
+
+    def set_bucket_groups(self, first_buckets: Sequence[int]) -> None:
+        """Group g = buckets [first_buckets[g], first_buckets[g + 1]); an
+        empty list restores one group per bucket."""
+        if self.sync and self.marks > 0 and not self.finished:
+            raise ModelError(ERR_UNFINISHED, self._unready())
+        B = len(self.buckets)
+        firsts = list(first_buckets) if len(first_buckets) else list(range(B))
+        if B and (firsts[0] != 0 or any(not 0 <= f < B for f in firsts)
+                  or any(a >= b for a, b in zip(firsts, firsts[1:]))):
+            raise ModelError(ERR_INVALID)
+        if not B and firsts:
+            raise ModelError(ERR_INVALID)
+        self.group_first = firsts
+
+    def _group_end(self, first: int) -> int:
+        i = self.group_first.index(first)
+        return self.group_first[i + 1] if i + 1 < len(self.group_first) else len(self.buckets)
+
+    def _advance(self) -> List[int]:
+        out = []
+        while self.next_bucket < len(self.buckets):
+            end = self._group_end(self.next_bucket)
+            if any(self.pending[b] for b in range(self.next_bucket, end)):
+                break
+            out += list(range(self.next_bucket, end))
+            self.next_bucket = end
+        self.launched += out
+        return out
 
     def set_require_sync(self, flag: bool) -> None:
         self.require_sync = bool(flag)
@@ -137,12 +174,7 @@ class ReducerModel:
                 if q != p:
                     self._mark(q)
         self._mark(p)
-        out = []
-        while self.next_bucket < len(self.buckets) and self.pending[self.next_bucket] == 0:
-            out.append(self.next_bucket)
-            self.next_bucket += 1
-        self.launched += out
-        return out
+        return self._advance()
 
     def finish(self) -> List[int]:
         """Returns the buckets launched by finishing (only in a backward where
@@ -154,10 +186,7 @@ class ReducerModel:
         if self.find_unused and self.marks == 0 and len(self.globally_unused()) == self.P:
             for q in range(self.P):
                 self._mark(q)
-            while self.next_bucket < len(self.buckets) and self.pending[self.next_bucket] == 0:
-                out.append(self.next_bucket)
-                self.next_bucket += 1
-            self.launched += out
+            out = self._advance()
         if self.next_bucket < len(self.buckets):
             raise ModelError(ERR_NOT_READY, self._unready())
         self.finished = True
@@ -178,3 +207,15 @@ def comm_timeline(bucket_bytes: Sequence[float], bucket_ready: Sequence[float], 
         spans.append((start, end))
         prev_end = end
     return spans
+
+
+def comm_timeline_groups(bucket_bytes: Sequence[float], bucket_ready: Sequence[float],
+                         group_first: Sequence[int], alpha: float, beta: float) -> List[Tuple[float, float]]:
+    """comm_timeline for bucket groups: group g starts when all its buckets
+    are ready and group g-1 has ended, and costs one alpha plus beta times
+    the group's bytes. Returns (start, end) per group."""
+    B = len(bucket_bytes)
+    bounds = list(group_first) + [B]
+    sizes = [sum(bucket_bytes[bounds[g]:bounds[g + 1]]) for g in range(len(group_first))]
+    ready = [max(bucket_ready[bounds[g]:bounds[g + 1]]) for g in range(len(group_first))]
+    return comm_timeline(sizes, ready, alpha, beta)

@@ -176,3 +176,68 @@ def test_used_tables_accumulate_through_no_sync_passes():
     m.mark_ready(1)
     with pytest.raises(ModelError):            # too late once the backward has started
         m.set_local_used([[1, 1, 1], [1, 1, 1]])
+
+
+def test_one_group_over_both_buckets_is_the_one_bucket_case():
+    """Exercise 4 with both buckets in one group: one alpha, launched when
+    the last gradient is ready, as the lecture's single-bucket case."""
+    from oracle.reducer_model import comm_timeline_groups
+    g = golden("l15_exercise4_timeline.json")
+    ready = {int(k): v for k, v in g["grad_ready_ms"].items()}
+    m = ReducerModel(g["buckets"], 5)
+    m.set_bucket_groups([0])
+    out = {}
+    for p in sorted(ready, key=ready.get):
+        for b in m.mark_ready(p):
+            out[b] = ready[p]
+    assert out == {0: 5, 1: 5}                     # both wait for the last gradient
+    span = comm_timeline_groups(g["bucket_sizes_mb"], [out[0], out[1]], [0], g["alpha_ms"], g["beta_ms_per_mb"])
+    assert span[-1][1] == pytest.approx(g["step_one_bucket_ms"])
+    singles = comm_timeline_groups(g["bucket_sizes_mb"], [out[0], out[1]], [0, 1], g["alpha_ms"], g["beta_ms_per_mb"])
+    assert singles == comm_timeline(g["bucket_sizes_mb"], [out[0], out[1]], g["alpha_ms"], g["beta_ms_per_mb"])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_groups_launch_whole_and_in_order(seed):
+    rng = random.Random(seed)
+    P = rng.randint(1, 40)
+    plan = plan_buckets([rng.randint(0, 50) * 4 for _ in range(P)], REVERSE, cap=rng.choice([0, 16, 64, 256]),
+                        first_cap=16)
+    B = plan.n_buckets
+    firsts = [0] + sorted(rng.sample(range(1, B), rng.randint(0, B - 1))) if B > 1 else [0]
+    m = ReducerModel(plan.buckets, P)
+    m.set_bucket_groups(firsts)
+    bounds = firsts + [B]
+    order = list(range(P))
+    rng.shuffle(order)
+    seen = set()
+    for p in order:
+        seen.add(p)
+        out = m.mark_ready(p)
+        if out:
+            # whole groups only: starts and ends on group boundaries
+            assert out[0] in firsts and out[-1] + 1 in bounds
+            for b in out:
+                assert set(plan.buckets[b]) <= seen
+    assert m.launched == list(range(B))
+    m.finish()
+
+
+def test_group_rules():
+    plan = plan_buckets([4] * 6, REVERSE, cap=8, first_cap=8)   # 3 buckets
+    m = ReducerModel(plan.buckets, 6)
+    for bad in ([1], [0, 0], [0, 2, 1], [0, 3]):
+        with pytest.raises(ModelError) as e:
+            m.set_bucket_groups(bad)
+        assert e.value.code == ERR_INVALID
+    m.set_bucket_groups([0, 2])
+    assert m.mark_ready(5) == [] and m.mark_ready(4) == []     # bucket 0 ready, group {0,1} is not
+    assert m.mark_ready(3) == [] and m.mark_ready(2) == [0, 1]
+    with pytest.raises(ModelError) as e:
+        m.set_bucket_groups([])
+    assert e.value.code == ERR_UNFINISHED
+    assert m.mark_ready(1) == [] and m.mark_ready(0) == [2]
+    m.finish()
+    m.set_bucket_groups([])
+    m.prepare_for_backward()
+    assert m.mark_ready(5) == [] and m.mark_ready(4) == [0]
