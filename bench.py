@@ -276,6 +276,21 @@ def run_sweep(args):
                    "overlapped_step_ms": round(t_ov * 1e3, 3),
                    "serial_step_ms": round(t_se * 1e3, 3),
                    "exposed_ms": round((t_ov - t_bw) * 1e3, 3)}
+            if args.sweep_group_mib > 0 and s.plan.n_buckets > 1:
+                # bucket groups of at least sweep_group_mib: one launch per group
+                import bucketed_gradient_all_amd as ddp
+                firsts = ddp.groups_by_bytes(s.bucket_bytes, args.sweep_group_mib << 20)
+                ddp.ddp_set_bucket_groups(s.r, firsts)
+                s.timed(2, per_bucket=True)
+                t_gpb = s.timed(k, per_bucket=True) / k
+                s.timed(1, backward_us=us)
+                t_gov = s.timed(args.overlap_steps, backward_us=us) / args.overlap_steps
+                ddp.ddp_set_bucket_groups(s.r, [])
+                row.update({"group_min_mib": args.sweep_group_mib, "groups": len(firsts),
+                            "grouped_per_bucket_ready_ms": round(t_gpb * 1e3, 4),
+                            "grouped_per_bucket_ready_GBps": round(nbytes / t_gpb / 1e9, 1),
+                            "grouped_overlapped_step_ms": round(t_gov * 1e3, 3),
+                            "grouped_exposed_ms": round((t_gov - t_bw) * 1e3, 3)})
             log(json.dumps(row))
             rows.append(row)
             s.close()
@@ -307,6 +322,8 @@ def main():
     ap.add_argument("--sweep-worlds", default="2,4,8,16,32")
     ap.add_argument("--sweep-caps", default="0,1,5,10,25,50,100,200")
     ap.add_argument("--sweep-out", default="")
+    ap.add_argument("--sweep-group-mib", type=int, default=0,
+                    help="also measure bucket groups of at least this many MiB (0: off)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this size (for HBM counter calibration) and exit")
     args = ap.parse_args()

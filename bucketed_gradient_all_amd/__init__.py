@@ -136,6 +136,7 @@ def lib():
             "ddp_set_require_sync": [P, I32],
             "ddp_set_local_used": [P, P],
             "ddp_register_builtin_hook": [P, I32],
+            "ddp_set_bucket_groups": [P, P, I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -311,6 +312,24 @@ def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> No
         return
     r._hook = HOOK_FN(lambda ctx, b: int(fn(b)))
     _check(lib().ddp_register_comm_hook(r.handle, r._hook, None))
+
+
+def ddp_set_bucket_groups(r: Reducer, first_buckets: Sequence[int]) -> None:
+    """first_buckets: the first bucket of every group (empty: one group per bucket)."""
+    arr = np.ascontiguousarray(np.asarray(list(first_buckets), dtype=np.int32))
+    _check(lib().ddp_set_bucket_groups(r.handle, arr.ctypes.data if arr.size else None, int(arr.size)))
+
+
+def groups_by_bytes(bucket_bytes: Sequence[int], min_group_bytes: int) -> List[int]:
+    """First buckets of consecutive groups of at least min_group_bytes each
+    (the last group may be smaller)."""
+    firsts, acc = [], min_group_bytes
+    for b, nb in enumerate(bucket_bytes):
+        if acc >= min_group_bytes:
+            firsts.append(b)
+            acc = 0
+        acc += int(nb)
+    return firsts
 
 
 def ddp_register_builtin_hook(r: Reducer, hook: int) -> None:

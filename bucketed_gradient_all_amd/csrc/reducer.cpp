@@ -235,6 +235,11 @@ struct ddp_reducer {
     uint64_t *used_dev = nullptr;         // device masks inside the workspace
     // per-iteration state [DDP-ch17 §17.12, §17.16]
     std::vector<int32_t> pending;
+    // bucket groups [MegatronDDP §3]: group g = buckets [group_first[g],
+    // group_first[g + 1]), issued as one launch once all of them are ready
+    std::vector<int32_t> group_first;     // [G + 1], last entry B
+    std::vector<int32_t> group_of;        // [B]
+    std::vector<int32_t> group_pending;   // [G] gradients the group still waits for
     std::vector<uint8_t> ready;
     std::vector<int32_t> ready_order;
     int32_t next = 0;
@@ -246,6 +251,7 @@ struct ddp_reducer {
         masks_uploaded = false;
         pending.resize(pv.B);
         for (int b = 0; b < pv.B; ++b) pending[b] = int32_t(pv.members[b].size());
+        count_groups();
         ready.assign(pv.P, 0);
         ready_order.clear();
         next = 0;
@@ -260,6 +266,31 @@ struct ddp_reducer {
         return out;
     }
     bool in_iteration() const { return sync && marks > 0 && !finished; }
+
+    void set_groups(const int32_t *first, int32_t n)
+    {
+        group_first.clear();
+        if (first)
+            group_first.assign(first, first + n);
+        else
+            for (int32_t b = 0; b < pv.B; ++b) group_first.push_back(b);
+        group_first.push_back(pv.B);
+        group_of.resize(pv.B);
+        for (size_t g = 0; g + 1 < group_first.size(); ++g)
+            for (int32_t b = group_first[g]; b < group_first[g + 1]; ++b) group_of[b] = int32_t(g);
+    }
+
+    void count_groups()
+    {
+        group_pending.assign(group_first.size() - 1, 0);
+        for (int b = 0; b < pv.B; ++b) group_pending[group_of[b]] += pending[b];
+    }
+
+    // moves next past every group that is complete, in order
+    void advance()
+    {
+        while (next < pv.B && group_pending[group_of[next]] == 0) next = group_first[group_of[next] + 1];
+    }
 
     // the per-gradient replica masks of this synchronization window
     void compute_masks()
@@ -377,7 +408,9 @@ void mark_state(ddp_reducer *r, int32_t param)
     r->ready[param] = 1;
     r->ready_order.push_back(param);
     ++r->marks;
-    --r->pending[r->pv.bucket_of[param]];
+    const int32_t b = r->pv.bucket_of[param];
+    --r->pending[b];
+    --r->group_pending[r->group_of[b]];
 }
 
 int mark_one(ddp_reducer *r, int32_t param)
@@ -395,7 +428,7 @@ int mark_one(ddp_reducer *r, int32_t param)
         return fail(DDP_ERR_ALREADY_READY,
                     "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
     mark_state(r, param);
-    while (r->next < r->pv.B && r->pending[r->next] == 0) ++r->next;
+    r->advance();
     return DDP_OK;
 }
 
@@ -615,6 +648,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         }
     }
     if (pv.find_unused) r->window.assign(size_t(pv.W) * pv.P, 0);
+    r->set_groups(nullptr, 0);
     r->reset();
     *out = r;
     return DDP_OK;
@@ -696,7 +730,7 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
         if (all_unused) {
             const int32_t b0 = r->next;
             for (int32_t q = 0; q < r->pv.P; ++q) mark_state(r, q);
-            while (r->next < r->pv.B && r->pending[r->next] == 0) ++r->next;
+            r->advance();
             int lrc = launch_buckets(r, b0, r->next);
             if (lrc != DDP_OK) return lrc;
         }
@@ -742,6 +776,24 @@ int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     r->hook = fn;
     r->hook_ctx = ctx;
+    return DDP_OK;
+}
+
+int ddp_set_bucket_groups(ddp_reducer *r, const int32_t *first_bucket, int32_t n_groups)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (r->in_iteration())
+        return fail(DDP_ERR_UNFINISHED, "cannot regroup buckets while a backward is in flight");
+    if (n_groups < 0 || (n_groups > 0 && !first_bucket)) return fail(DDP_ERR_INVALID, "bad group list");
+    if (n_groups > 0) {
+        if (r->pv.B == 0 || first_bucket[0] != 0) return fail(DDP_ERR_INVALID, "the first group must start at bucket 0");
+        for (int32_t g = 0; g < n_groups; ++g) {
+            if (first_bucket[g] < 0 || first_bucket[g] >= r->pv.B || (g > 0 && first_bucket[g] <= first_bucket[g - 1]))
+                return fail(DDP_ERR_INVALID, "group starts must be strictly increasing bucket indices");
+        }
+    }
+    r->set_groups(n_groups > 0 ? first_bucket : nullptr, n_groups);
+    r->count_groups();
     return DDP_OK;
 }
 

@@ -236,6 +236,20 @@ int ddp_set_local_used(ddp_reducer *r, const uint8_t *used);
 typedef int (*ddp_comm_hook_fn)(void *ctx, int32_t bucket);
 int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx);
 
+/* Bucket groups [MegatronDDP §3]: consecutive buckets whose reductions are
+ * issued together, as one launch, once every bucket of the group is ready
+ * and every earlier group was issued. This trades overlap for fewer launches
+ * (one launch overhead per group instead of per bucket), which pays at small
+ * caps. first_bucket: [n_groups] strictly increasing bucket indices, the
+ * first 0; group g = [first_bucket[g], first_bucket[g+1]) (the last group
+ * runs to the end). n_groups = 0 (first_bucket may be NULL) restores the
+ * default, one group per bucket. The reducer keeps its own copy.
+ * Independently of groups, buckets completed by one ready call
+ * (ddp_mark_ready_many) always go out as one launch.
+ * Errors: DDP_ERR_INVALID for a malformed list; DDP_ERR_UNFINISHED while a
+ * backward is in flight. */
+int ddp_set_bucket_groups(ddp_reducer *r, const int32_t *first_bucket, int32_t n_groups);
+
 /* Built-in communication hooks [DDP-ch17 §17.9]: the arithmetic every
  * bucket reduction of this reducer uses (the reducer's own launches and
  * ddp_bucket_reduce, also from a callback hook).

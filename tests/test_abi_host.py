@@ -390,3 +390,71 @@ def test_builtin_hook_rules():
     ddp.ddp_finish(r)
     ddp.ddp_register_builtin_hook(r, ddp.DDP_HOOK_BF16_COMPRESS)   # between iterations: allowed
     ddp.ddp_reducer_destroy(r)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_bucket_groups_match_oracle(seed):
+    rng = random.Random(seed)
+    P = rng.randint(1, 30)
+    numel = [rng.randint(0, 40) for _ in range(P)]
+    r, plan, log = host_reducer(numel, rng.choice([0, 16, 64, 400]), rng.choice([16, 64]))
+    B = plan.n_buckets
+    model = ReducerModel(plan.buckets(), P)
+    for it in range(3):
+        firsts = [0] + sorted(rng.sample(range(1, B), rng.randint(0, B - 1))) if B > 1 else [0]
+        if it == 2:
+            firsts = []
+        ddp.ddp_set_bucket_groups(r, firsts)
+        model.set_bucket_groups(firsts)
+        ddp.ddp_prepare_for_backward(r)
+        model.prepare_for_backward()
+        order = list(range(P))
+        rng.shuffle(order)
+        i = 0
+        while i < P:
+            k = rng.randint(1, 4)
+            chunk = order[i:i + k]
+            before = len(log)
+            ddp.ddp_mark_ready_many(r, chunk)
+            want = []
+            for p in chunk:
+                want += model.mark_ready(p)
+            assert log[before:] == want
+            assert ddp.ddp_get_launched(r) == model.next_bucket
+            i += k
+        ddp.ddp_finish(r)
+        model.finish()
+    ddp.ddp_reducer_destroy(r)
+
+
+def test_bucket_group_errors():
+    r, plan, log = host_reducer([1] * 6, 8, 8)     # 3 buckets of 2 gradients each
+    assert plan.n_buckets == 3
+    for bad in ([1], [0, 0], [0, 2, 1], [0, 3], [-1]):
+        with pytest.raises(ddp.DDPError) as e:
+            ddp.ddp_set_bucket_groups(r, bad)
+        assert e.value.code == ddp.DDP_ERR_INVALID
+    ddp.ddp_set_bucket_groups(r, [0, 2])
+    ddp.ddp_prepare_for_backward(r)
+    ddp.ddp_mark_ready(r, 5)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_set_bucket_groups(r, [])
+    assert e.value.code == ddp.DDP_ERR_UNFINISHED
+    for p in (4, 3, 2):
+        ddp.ddp_mark_ready(r, p)
+    assert log == [0, 1]
+    ddp.ddp_mark_ready_many(r, [1, 0])
+    assert log == [0, 1, 2]
+    ddp.ddp_finish(r)
+    ddp.ddp_set_bucket_groups(r, [])
+    with pytest.raises(ddp.DDPError) as e:     # still ready until the next prepare
+        ddp.ddp_mark_ready(r, 0)
+    assert e.value.code == ddp.DDP_ERR_ALREADY_READY
+    ddp.ddp_reducer_destroy(r)
+
+
+def test_groups_by_bytes():
+    assert ddp.groups_by_bytes([10, 10, 10, 10, 10], 25) == [0, 3]
+    assert ddp.groups_by_bytes([30, 1, 1], 25) == [0, 1]
+    assert ddp.groups_by_bytes([1] * 4, 0) == [0, 1, 2, 3]
+    assert ddp.groups_by_bytes([], 5) == []
