@@ -215,7 +215,9 @@ struct ddp_reducer {
     int32_t builtin_hook = DDP_HOOK_ALLREDUCE;   // kernel family of every launch
     KernelTables tables{};
     hipStream_t compute = nullptr, comm = nullptr;
-    hipEvent_t ev_ready = nullptr, ev_done = nullptr;
+    // stream-to-stream events on one device need only device-scope release;
+    // ev_host (system scope) is what a host-blocking finish waits on
+    hipEvent_t ev_ready = nullptr, ev_done = nullptr, ev_host = nullptr;
     bool timing = false;
     std::vector<hipEvent_t> t0, t1;       // event pool, reused across record lists
     std::vector<int32_t> timed_bucket;    // first bucket of each recorded launch
@@ -444,11 +446,12 @@ void destroy_events(ddp_reducer *r)
     r->stage = nullptr;
     if (r->ev_ready) (void)hipEventDestroy(r->ev_ready);
     if (r->ev_done) (void)hipEventDestroy(r->ev_done);
+    if (r->ev_host) (void)hipEventDestroy(r->ev_host);
     for (auto e : r->t0)
         if (e) (void)hipEventDestroy(e);
     for (auto e : r->t1)
         if (e) (void)hipEventDestroy(e);
-    r->ev_ready = r->ev_done = nullptr;
+    r->ev_ready = r->ev_done = r->ev_host = nullptr;
     r->t0.clear();
     r->t1.clear();
 }
@@ -634,8 +637,10 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
             r->used_dev = reinterpret_cast<uint64_t *>(ws + lay.used_off);
             r->tables.used = r->used_dev;
         }
-        e = hipEventCreateWithFlags(&r->ev_ready, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_done, hipEventDisableTiming);
+        const unsigned local = hipEventDisableTiming | hipEventDisableSystemFence;
+        e = hipEventCreateWithFlags(&r->ev_ready, local);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_done, local);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_host, hipEventDisableTiming);
         if (e == hipSuccess && pv.find_unused && pv.P > 0) {
             e = hipHostMalloc(reinterpret_cast<void **>(&r->stage), 2 * sizeof(uint64_t) * pv.P);
             for (int k = 0; k < 2 && e == hipSuccess; ++k)
@@ -739,9 +744,15 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
         return fail(DDP_ERR_NOT_READY,
                     "buckets still wait for gradients never marked ready: " + list_params(r->unready()));
     if (r->device) {
-        hipError_t e = hipEventRecord(r->ev_done, r->comm);
-        if (e == hipSuccess && r->compute != r->comm) e = hipStreamWaitEvent(r->compute, r->ev_done, 0);
-        if (e == hipSuccess && host_blocking) e = hipEventSynchronize(r->ev_done);
+        hipError_t e = hipSuccess;
+        if (r->compute != r->comm) {
+            e = hipEventRecord(r->ev_done, r->comm);
+            if (e == hipSuccess) e = hipStreamWaitEvent(r->compute, r->ev_done, 0);
+        }
+        if (e == hipSuccess && host_blocking) {
+            e = hipEventRecord(r->ev_host, r->comm);
+            if (e == hipSuccess) e = hipEventSynchronize(r->ev_host);
+        }
         if (e != hipSuccess) return hip_fail("finish", e);
     }
     r->finished = true;
