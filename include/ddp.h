@@ -16,13 +16,18 @@
  * On one GPU the W data-parallel replicas are W gradient buffers resident in
  * HBM, so a bucket "all-reduce" is one streaming kernel: it reads the bucket
  * from all W replicas, scales by 1/W, sums in the ring all-reduce's order and
- * writes the identical mean back to all W replicas' flat buffers.
+ * writes the identical mean back to all W replicas' flat buffers (or, as a
+ * reduce-scatter, each ring chunk to its owner only). Built-in bf16 / fp16
+ * compression hooks change that arithmetic; unused-parameter detection
+ * masks replicas out per gradient.
  *
  * Memory ownership: the caller allocates and owns every device buffer
  * (gradients, flat buffers, workspace) and both streams; they must stay
  * valid until ddp_reducer_destroy returns. The library copies the plan and
  * the pointer tables into its own host memory at creation and writes its
  * device tables into the caller's workspace; it allocates no device memory.
+ * With unused-parameter detection it allocates one pinned host staging
+ * buffer of 16 * P bytes (hipHostMalloc), freed by ddp_reducer_destroy.
  *
  * Threading: a reducer is used from one thread at a time (hooks fire from
  * one thread, [DDP-ch17 §17.12]). ddp_last_error() text is per thread.
@@ -164,11 +169,15 @@ int ddp_prepare_for_backward(ddp_reducer *r);
 
 /* The gradient-ready hook for gradient `param` [DDP-ch17 §17.3, §17.12; L15
  * §2.3; MegatronDDP §2]: decrements its bucket's pending count, then launches
- * buckets strictly by index, from the first unlaunched one, for as long as
- * their counts are zero. A launch makes the comm stream wait for the work
- * queued so far on the compute stream (no wait is enqueued when that stream
- * has already drained), then runs the registered hook or, by default, the
- * bucket reduction on the comm stream. May launch 0..B buckets.
+ * bucket groups (ddp_set_bucket_groups; by default one bucket each) strictly
+ * in order, from the first unlaunched one, for as long as every count in the
+ * group is zero. With unused-parameter detection, the backward's first mark
+ * also marks every gradient no replica used. A launch makes the comm stream
+ * wait for the work queued so far on the compute stream (no wait is enqueued
+ * when that stream has already drained), then runs the registered hook once
+ * per bucket or, by default, one bucket-reduce kernel over the launched
+ * buckets on the comm stream. May launch 0..B buckets. Inside no_sync the
+ * call only checks the index (see ddp_set_require_sync).
  * Errors: DDP_ERR_INVALID (index out of range), DDP_ERR_ALREADY_READY,
  * DDP_ERR_HIP, DDP_ERR_HOOK; a launch that failed still counts as issued. */
 int ddp_mark_ready(ddp_reducer *r, int32_t param);
@@ -197,7 +206,11 @@ int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_
  * fp32 add rounded to nearest even: the value the ring reduce-scatter leaves
  * for chunk c [DDP-ch17 §17.4, §17.9; MegatronDDP §3]. acc is written to
  * element e of all W flat buffers (the all-gather), or, for
- * DDP_REDUCE_SCATTER, to replica c's flat buffer only. */
+ * DDP_REDUCE_SCATTER, to replica c's flat buffer only. That is the default
+ * hook's arithmetic; a compression hook (ddp_register_builtin_hook) changes
+ * the term and every add as described there. With unused-parameter
+ * detection the reduction applies the replica masks last uploaded (all
+ * replicas before the first synchronized backward's first launch). */
 int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
 
 /* End of backward [DDP-ch17 §17.41; MegatronDDP §5]: checks that every bucket
