@@ -458,3 +458,14 @@ def test_groups_by_bytes():
     assert ddp.groups_by_bytes([30, 1, 1], 25) == [0, 1]
     assert ddp.groups_by_bytes([1] * 4, 0) == [0, 1, 2, 3]
     assert ddp.groups_by_bytes([], 5) == []
+
+
+def test_unused_detection_limits_world_to_64():
+    pb = [4, 4]
+    plan = ddp.ddp_plan_buckets(pb, ddp.DDP_ORDER_REVERSE, 8, 8)
+    ok = ddp.Desc(64, [1, 1], plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, find_unused=True)
+    ddp.ddp_reducer_destroy(ddp.ddp_reducer_create(ok))
+    bad = ddp.Desc(65, [1, 1], plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, find_unused=True)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_reducer_create(bad)
+    assert e.value.code == ddp.DDP_ERR_INVALID

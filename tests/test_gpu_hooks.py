@@ -183,3 +183,19 @@ def test_megatron_llama1b_sampled_with_bf16_hook():
     assert_bits(got, want, "megatron_llama1b bf16 hook sampled")
     assert run.replicas_equal_device()
     run.close()
+
+
+@pytest.mark.parametrize("hook", [0, BF16_HOOK, FP16_HOOK])
+def test_hundred_replicas_generic_kernel(hook):
+    """W = 100 runs the generic kernel (replicas eight at a time)."""
+    from synth.workloads import Workload, DIST_NORMAL
+    wl = Workload("w100", [(5000,), (33,), (12289,)], world=100, cap_bytes=30000, first_cap_bytes=30000,
+                  dist=DIST_NORMAL, sigma=1.0, seed=100)
+    run = hooked(Run(wl), hook)
+    run.step()
+    if hook:
+        check_hook_full(run, hook)
+    else:
+        from test_gpu_parity import check_full
+        check_full(run)
+    run.close()

@@ -148,3 +148,23 @@ def test_resnet50_with_unused_branch_bit_exact():
     ddp.ddp_finish(run.r, host_blocking=True)
     check(run, used, before)
     run.close()
+
+
+def test_sixty_four_replicas_is_the_mask_limit():
+    """W = 64 fills the 64-bit replica mask; every bit position is exercised."""
+    from synth.workloads import Workload, DIST_UNIFORM
+    W = 64
+    wl = Workload("w64_unused", [(700,), (64,), (1500,), (3,)], world=W, cap_bytes=4000, first_cap_bytes=4000,
+                  dist=DIST_UNIFORM, seed=64)
+    P = len(wl.numel)
+    run = URun(wl)
+    used = [[(w + p) % 3 != 0 for p in range(P)] for w in range(W)]
+    used[63] = [1] * P
+    before = [run.flat_host(w) for w in range(W)]
+    ddp = run.ddp
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_set_local_used(run.r, used)
+    ddp.ddp_mark_ready_many(run.r, list(range(P - 1, -1, -1)))
+    ddp.ddp_finish(run.r, host_blocking=True)
+    check(run, used, before)
+    run.close()
