@@ -137,6 +137,8 @@ def lib():
             "ddp_set_local_used": [P, P],
             "ddp_register_builtin_hook": [P, I32],
             "ddp_set_bucket_groups": [P, P, I32],
+            "ddp_set_workgroups_per_cu": [P, I32],
+            "ddp_get_launch_lds": [P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -330,6 +332,16 @@ def groups_by_bytes(bucket_bytes: Sequence[int], min_group_bytes: int) -> List[i
             acc = 0
         acc += int(nb)
     return firsts
+
+
+def ddp_set_workgroups_per_cu(r: Reducer, n: int) -> None:
+    _check(lib().ddp_set_workgroups_per_cu(r.handle, int(n)))
+
+
+def ddp_get_launch_lds(r: Reducer) -> int:
+    out = ctypes.c_int32()
+    _check(lib().ddp_get_launch_lds(r.handle, ctypes.byref(out)))
+    return out.value
 
 
 def ddp_register_builtin_hook(r: Reducer, hook: int) -> None:

@@ -19,6 +19,18 @@ constexpr int unroll_for(int W)
     return W <= 4 ? 4 : (W <= 8 ? 2 : 1);
 }
 
+// Workgroups of one launch resident per CU (0: as many as registers allow).
+// The kernel uses no LDS; the launch reserves LDS only so that the hardware
+// dispatcher keeps at most this many workgroups on a CU. Fewer tiles in
+// flight keep each of the 2W streams' in-flight window narrow (a few MiB
+// across the chip), which measured 4-8% faster than full occupancy for
+// W >= 3; the reduce-scatter (one write stream) and U = 1 (smaller tiles)
+// do best at two per CU; W <= 2 (four streams) at full occupancy.
+constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter)
+{
+    return W <= 2 ? 0 : ((reduce_scatter || unroll_for(W) == 1) ? 2 : 1);
+}
+
 // Elements one workgroup covers (one tile).
 constexpr int64_t tile_elems(int W)
 {
@@ -66,11 +78,13 @@ struct Scale {
 //   launch_mean:       the fp32 mean (no communication hook)
 //   launch_bf16_hook:  through the bf16 compression hook
 //   launch_fp16_hook:  through the fp16 compression hook
+// lds_bytes: LDS each workgroup reserves (unused by the kernel; it bounds the
+// workgroups resident per CU, see auto_workgroups_per_cu).
 hipError_t launch_mean(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                       int32_t tile_begin, int32_t n_tiles, hipStream_t s);
+                       int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
 hipError_t launch_bf16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                            int32_t tile_begin, int32_t n_tiles, hipStream_t s);
+                            int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
 hipError_t launch_fp16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                            int32_t tile_begin, int32_t n_tiles, hipStream_t s);
+                            int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
 
 }  // namespace ddp

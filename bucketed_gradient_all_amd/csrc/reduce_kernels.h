@@ -420,53 +420,53 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
 
 template <int W, int MODE, int HOOK>
 hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc, bool rs,
-                        hipStream_t st)
+                        unsigned lds, hipStream_t st)
 {
     const dim3 g(n_tiles), b(kThreads);
     if (t.used) {
         if (rs)
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true>), g, b, 0, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true>), g, b, lds, st, t, tile_begin, sc);
         else
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, true>), g, b, 0, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, true>), g, b, lds, st, t, tile_begin, sc);
     } else {
         if (rs)
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, false>), g, b, 0, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, false>), g, b, lds, st, t, tile_begin, sc);
         else
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, false>), g, b, 0, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, false>), g, b, lds, st, t, tile_begin, sc);
     }
     return hipGetLastError();
 }
 
 template <int MODE, int HOOK>
 hipError_t dispatch_w(int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc,
-                      hipStream_t st)
+                      unsigned lds, hipStream_t st)
 {
     switch (W) {
-    case 1: return launch_fixed<1, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 2: return launch_fixed<2, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 3: return launch_fixed<3, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 4: return launch_fixed<4, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 5: return launch_fixed<5, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 6: return launch_fixed<6, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 7: return launch_fixed<7, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 8: return launch_fixed<8, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 16: return launch_fixed<16, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
-    case 32: return launch_fixed<32, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, st);
+    case 1: return launch_fixed<1, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 2: return launch_fixed<2, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 3: return launch_fixed<3, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 4: return launch_fixed<4, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 5: return launch_fixed<5, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 6: return launch_fixed<6, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 7: return launch_fixed<7, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 8: return launch_fixed<8, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 16: return launch_fixed<16, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 32: return launch_fixed<32, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
     default:
-        hipLaunchKernelGGL((reduce_generic<MODE, HOOK>), dim3(n_tiles), dim3(kThreads), 0, st, t, tile_begin, sc, W,
-                           rs ? 1 : 0);
+        hipLaunchKernelGGL((reduce_generic<MODE, HOOK>), dim3(n_tiles), dim3(kThreads), lds, st, t, tile_begin, sc,
+                           W, rs ? 1 : 0);
         return hipGetLastError();
     }
 }
 
 template <int HOOK>
 hipError_t dispatch_mode(int mode, int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles,
-                         const Scale &sc, hipStream_t st)
+                         const Scale &sc, unsigned lds, hipStream_t st)
 {
     switch (mode) {
-    case MODE_COPY: return dispatch_w<MODE_COPY, HOOK>(W, rs, t, tile_begin, n_tiles, sc, st);
-    case MODE_VIEW: return dispatch_w<MODE_VIEW, HOOK>(W, rs, t, tile_begin, n_tiles, sc, st);
-    case MODE_BF16: return dispatch_w<MODE_BF16, HOOK>(W, rs, t, tile_begin, n_tiles, sc, st);
+    case MODE_COPY: return dispatch_w<MODE_COPY, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st);
+    case MODE_VIEW: return dispatch_w<MODE_VIEW, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st);
+    case MODE_BF16: return dispatch_w<MODE_BF16, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -213,6 +213,19 @@ struct ddp_reducer {
     bool device = false;
     ddp::Scale scale{1.0f, 1.0f, 0};
     int32_t builtin_hook = DDP_HOOK_ALLREDUCE;   // kernel family of every launch
+    int32_t workgroups_per_cu = 0;               // 0: automatic, < 0: no cap, 1..8: cap
+    int lds_per_cu = 0, lds_per_block = 0;       // the device's LDS sizes (bytes)
+
+    // LDS each launch reserves so that at most k of its workgroups share a CU
+    unsigned launch_lds() const
+    {
+        const int k = workgroups_per_cu == 0 ? ddp::auto_workgroups_per_cu(pv.W, pv.reduce_scatter)
+                                             : (workgroups_per_cu < 0 ? 0 : workgroups_per_cu);
+        if (k <= 0 || lds_per_cu <= 0) return 0;
+        int bytes = lds_per_cu / (k + 1) + 2048;   // k fit, k + 1 do not
+        bytes = (bytes + 255) / 256 * 256;
+        return unsigned(std::min(bytes, lds_per_block));
+    }
     KernelTables tables{};
     hipStream_t compute = nullptr, comm = nullptr;
     // stream-to-stream events on one device need only device-scope release;
@@ -331,15 +344,17 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
     }
     const int32_t tile0 = r->pv.tile_begin[b0];
     const int32_t tiles = r->pv.tile_begin[b1 - 1] + r->pv.tile_count[b1 - 1] - tile0;
+    const unsigned lds = r->launch_lds();
+    const PlanView &pv = r->pv;
     switch (r->builtin_hook) {
     case DDP_HOOK_BF16_COMPRESS:
-        e = ddp::launch_bf16_hook(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+        e = ddp::launch_bf16_hook(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
         break;
     case DDP_HOOK_FP16_COMPRESS:
-        e = ddp::launch_fp16_hook(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+        e = ddp::launch_fp16_hook(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
         break;
     default:
-        e = ddp::launch_mean(r->pv.mode, r->pv.W, r->pv.reduce_scatter, r->scale, r->tables, tile0, tiles, s);
+        e = ddp::launch_mean(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
         break;
     }
     if (e != hipSuccess) return hip_fail("bucket reduce launch", e);
@@ -637,6 +652,12 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
             r->used_dev = reinterpret_cast<uint64_t *>(ws + lay.used_off);
             r->tables.used = r->used_dev;
         }
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&r->lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&r->lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         const unsigned local = hipEventDisableTiming | hipEventDisableSystemFence;
         e = hipEventCreateWithFlags(&r->ev_ready, local);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_done, local);
@@ -649,7 +670,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         if (e != hipSuccess) {
             destroy_events(r);
             delete r;
-            return hip_fail("hipEventCreate", e);
+            return hip_fail("reducer setup (device attributes, events, staging)", e);
         }
     }
     if (pv.find_unused) r->window.assign(size_t(pv.W) * pv.P, 0);
@@ -805,6 +826,21 @@ int ddp_set_bucket_groups(ddp_reducer *r, const int32_t *first_bucket, int32_t n
     }
     r->set_groups(n_groups > 0 ? first_bucket : nullptr, n_groups);
     r->count_groups();
+    return DDP_OK;
+}
+
+int ddp_set_workgroups_per_cu(ddp_reducer *r, int32_t n)
+{
+    if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (n > 8) return fail(DDP_ERR_INVALID, "workgroups per CU must be at most 8 (or 0: automatic, < 0: no cap)");
+    r->workgroups_per_cu = n;
+    return DDP_OK;
+}
+
+int ddp_get_launch_lds(const ddp_reducer *r, int32_t *lds_bytes)
+{
+    if (!r || !lds_bytes) return fail(DDP_ERR_INVALID, "NULL argument");
+    *lds_bytes = int32_t(r->launch_lds());
     return DDP_OK;
 }
 

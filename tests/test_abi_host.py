@@ -469,3 +469,14 @@ def test_unused_detection_limits_world_to_64():
     with pytest.raises(ddp.DDPError) as e:
         ddp.ddp_reducer_create(bad)
     assert e.value.code == ddp.DDP_ERR_INVALID
+
+
+def test_workgroups_per_cu_rules():
+    r, plan, log = host_reducer([1] * 4, 8, 8)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_set_workgroups_per_cu(r, 9)
+    assert e.value.code == ddp.DDP_ERR_INVALID
+    for n in (-1, 0, 1, 8):
+        ddp.ddp_set_workgroups_per_cu(r, n)
+        assert ddp.ddp_get_launch_lds(r) == 0      # no device: nothing to reserve
+    ddp.ddp_reducer_destroy(r)
