@@ -69,7 +69,7 @@ def measured_traffic(workload: str):
 
 
 class Session:
-    def __init__(self, wl, arena: bool = False):
+    def __init__(self, wl, arena: bool = False, stagger: int = 0):
         import numpy as np
         import torch
 
@@ -85,7 +85,7 @@ class Session:
         self.total = sum(bb) // 4
         self.bucket_bytes = bb
         t0 = time.perf_counter()
-        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena)
+        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena, stagger=stagger)
         log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
         self.compute = torch.cuda.Stream()
         self.comm = torch.cuda.Stream()
@@ -313,6 +313,8 @@ def main():
     ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
     ap.add_argument("--hook", default="none", choices=list(HOOKS),
                     help="built-in communication hook: the fp32 mean, or bf16 / fp16 compression")
+    ap.add_argument("--stagger", type=int, default=0,
+                    help="bytes by which replica w's buffers start w * stagger into their allocations")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-ms", type=float, default=20.0,
@@ -372,7 +374,7 @@ def main():
         wl.name += f"_{args.hook}hook"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
-    s = Session(wl)
+    s = Session(wl, stagger=args.stagger)
     import bucketed_gradient_all_amd as ddp
     ddp.ddp_register_builtin_hook(s.r, hook)
     bytes_per_step = wl.algorithmic_bytes()

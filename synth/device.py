@@ -26,13 +26,19 @@ SENTINEL = -1   # 0xFFFFFFFF: a NaN pattern the reduction never produces from fi
 
 class DeviceInputs:
     def __init__(self, wl: Workload, flat_offset_elems: Sequence[int], total_elems: int, device: str = "cuda",
-                 seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0, arena: bool = False):
+                 seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0, arena: bool = False,
+                 stagger: int = 0):
         """misalign: bytes added to the start of every other gradient tensor
         (to exercise unaligned sources); flat_shift: elements the flat
         buffers start past their allocation, one value or one per replica (to
         exercise unaligned outputs);
         arena: carve every buffer out of one allocation instead of one
-        allocation per buffer."""
+        allocation per buffer;
+        stagger: bytes (a multiple of 256) by which replica w's gradient and
+        flat buffers start w * stagger past their allocations, so that the W
+        replicas' copies of one element do not sit at the same offset in
+        same-size allocations (the HBM channel a line maps to depends on its
+        address)."""
         import torch
 
         self.wl = wl
@@ -55,7 +61,11 @@ class DeviceInputs:
             cur += (n * esz + shift + ALIGN - 1) // ALIGN * ALIGN
         self.grad_bytes = max(cur, ALIGN)
         self.grads = []
+        if stagger % ALIGN:
+            raise ValueError("stagger must be a multiple of 256 bytes")
+        self.stagger = stagger
         shifts = list(flat_shift) if isinstance(flat_shift, (list, tuple)) else [flat_shift] * W
+        shifts = [sh + w * stagger // 4 for w, sh in enumerate(shifts)]
         self.flat_shift = shifts
         flat_bytes = (4 * (max(self.total, 1) + max(shifts)) + ALIGN - 1) // ALIGN * ALIGN
         if arena:
@@ -72,7 +82,8 @@ class DeviceInputs:
                 base += flat_bytes
         else:
             if self.mode != IN_F32_VIEW:
-                self.grads = [torch.empty(self.grad_bytes, dtype=torch.uint8, device=device) for _ in range(W)]
+                self.grads = [torch.empty(self.grad_bytes + w * stagger, dtype=torch.uint8, device=device)
+                              [w * stagger:] for w in range(W)]
             self._flat_alloc = [torch.empty(flat_bytes // 4, dtype=torch.float32, device=device) for _ in range(W)]
         self.flat = [a[sh:sh + max(self.total, 1)] for a, sh in zip(self._flat_alloc, shifts)]
         self.refill()
