@@ -661,7 +661,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
             e = hipDeviceGetAttribute(&r->lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
         if (e == hipSuccess)
             e = hipDeviceGetAttribute(&r->lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-        e = hipEventCreateWithFlags(&r->ev_ready, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_ready, hipEventDisableTiming);
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&r->ev_done, hipEventDisableTiming | hipEventDisableSystemFence);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_host, hipEventDisableTiming);
