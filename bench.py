@@ -69,7 +69,7 @@ def measured_traffic(workload: str):
 
 
 class Session:
-    def __init__(self, wl, arena: bool = False, stagger: int = 0):
+    def __init__(self, wl, arena: bool = False, stagger: int = 0, backward_kind: str = "spin"):
         import numpy as np
         import torch
 
@@ -93,6 +93,8 @@ class Session:
                                   self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
                                   collective=wl.collective)
         self.order = np.arange(len(wl.numel) - 1, -1, -1, dtype=np.int32)
+        self.backward_kind = backward_kind
+        self._gemm = None
         self.members = [np.asarray(m, np.int32) for m in self.plan.buckets()]
 
     def step(self, backward_us: float = 0.0, serial: bool = False, per_bucket: bool = False,
@@ -103,13 +105,16 @@ class Session:
         backward on the compute stream, one piece per bucket in proportion to
         its bytes, each followed by that bucket's ready call (serial: the
         whole backward first, then the ready calls); backward_only: the
-        pieces alone, no reduction."""
+        pieces alone, no reduction. The pieces are a one-workgroup wall-clock
+        wait (backward_kind "spin": time passes, no resources are taken) or
+        bf16 GEMMs (backward_kind "gemm": they compete with the reduction
+        for CUs and HBM, as a real backward would)."""
         ddp = self.ddp
         if backward_only:
             import synth
             tot = float(sum(self.bucket_bytes)) or 1.0
             for b in range(len(self.members)):
-                synth.spin_dev(backward_us * self.bucket_bytes[b] / tot, self.compute.cuda_stream)
+                self._piece(backward_us * self.bucket_bytes[b] / tot)
             return
         ddp.ddp_prepare_for_backward(self.r)
         if backward_us <= 0 and not per_bucket:
@@ -123,10 +128,10 @@ class Session:
             cs = self.compute.cuda_stream
             for b, members in enumerate(self.members):
                 if not serial:
-                    synth.spin_dev(backward_us * self.bucket_bytes[b] / tot, cs)
+                    self._piece(backward_us * self.bucket_bytes[b] / tot)
                 elif b == 0:
                     for bb in range(len(self.members)):
-                        synth.spin_dev(backward_us * self.bucket_bytes[bb] / tot, cs)
+                        self._piece(backward_us * self.bucket_bytes[bb] / tot)
                 if not serial:
                     ddp.ddp_mark_ready_many(self.r, members)
             if serial:
@@ -140,6 +145,34 @@ class Session:
         del self.inputs
         self.torch.cuda.synchronize()
         self.torch.cuda.empty_cache()
+
+    def _piece(self, us: float):
+        """One piece of the synthetic backward on the compute stream."""
+        if self.backward_kind == "spin":
+            import synth
+            synth.spin_dev(us, self.compute.cuda_stream)
+            return
+        torch = self.torch
+        if self._gemm is None:
+            # bf16 GEMMs of 4096^3 on contiguous operands; time one to size the pieces
+            n = 4096
+            a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16).contiguous()
+            c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+            with torch.cuda.stream(self.compute):
+                for _ in range(3):
+                    torch.mm(a, b, out=c)
+                self.compute.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(20):
+                    torch.mm(a, b, out=c)
+                self.compute.synchronize()
+            self._gemm = (a, b, c, (time.perf_counter() - t0) / 20 * 1e6)
+            log(f"[bench] gemm backward: one 4096^3 bf16 GEMM = {self._gemm[3]:.1f} us")
+        a, b, c, t = self._gemm
+        with torch.cuda.stream(self.compute):
+            for _ in range(max(1, int(round(us / t)))):
+                torch.mm(a, b, out=c)
 
     def timed(self, steps: int, **kw):
         torch = self.torch
@@ -253,7 +286,9 @@ def run_sweep(args):
     for W in worlds:
         for cap in caps:
             wl = wls.sweep(W, cap)
-            s = Session(wl)
+            s = Session(wl, backward_kind=args.backward_kind)
+            import bucketed_gradient_all_amd as ddp
+            ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
             nbytes = wl.algorithmic_bytes()
             # size the timed region to about 50 ms
             t1 = s.timed(1, per_bucket=True)
@@ -320,6 +355,10 @@ def main():
     ap.add_argument("--backward-ms", type=float, default=20.0,
                     help="synthetic backward for the overlap measurement (0 disables it)")
     ap.add_argument("--overlap-steps", type=int, default=5)
+    ap.add_argument("--backward-kind", default="spin", choices=["spin", "gemm"],
+                    help="synthetic backward: a one-workgroup wait, or bf16 GEMMs that compete for the GPU")
+    ap.add_argument("--workgroups-per-cu", type=int, default=0,
+                    help="reduction workgroups per CU (0: the library's automatic choice, -1: no cap)")
     ap.add_argument("--sweep", action="store_true", help="run the bucket-size sweep instead of one workload")
     ap.add_argument("--sweep-worlds", default="2,4,8,16,32")
     ap.add_argument("--sweep-caps", default="0,1,5,10,25,50,100,200")
@@ -374,9 +413,10 @@ def main():
         wl.name += f"_{args.hook}hook"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
-    s = Session(wl, stagger=args.stagger)
+    s = Session(wl, stagger=args.stagger, backward_kind=args.backward_kind)
     import bucketed_gradient_all_amd as ddp
     ddp.ddp_register_builtin_hook(s.r, hook)
+    ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
     bytes_per_step = wl.algorithmic_bytes()
 
     for _ in range(args.warmup):
@@ -434,9 +474,13 @@ def main():
         s.step(backward_us=us)
         t_ov = s.timed(args.overlap_steps, backward_us=us) / args.overlap_steps
         t_se = s.timed(args.overlap_steps, backward_us=us, serial=True) / args.overlap_steps
-        overlap = {"backward_ms": args.backward_ms, "step_ms_overlapped": round(t_ov * 1e3, 3),
+        s.timed(1, backward_us=us, backward_only=True)
+        t_bw = s.timed(args.overlap_steps, backward_us=us, backward_only=True) / args.overlap_steps
+        overlap = {"backward_ms": args.backward_ms, "backward_kind": args.backward_kind,
+                   "backward_alone_ms": round(t_bw * 1e3, 3),
+                   "step_ms_overlapped": round(t_ov * 1e3, 3),
                    "step_ms_serial": round(t_se * 1e3, 3),
-                   "exposed_ms": round(t_ov * 1e3 - args.backward_ms, 3),
+                   "exposed_ms": round((t_ov - t_bw) * 1e3, 3),
                    "reduce_ms_alone": round(step_s * 1e3, 3)}
 
     cpu = None
@@ -466,6 +510,8 @@ def main():
                    "input_mode": MODE_NAMES[wl.input_mode], "bytes_per_step": bytes_per_step,
                    "collective": "reduce_scatter" if wl.collective == wls.REDUCE_SCATTER else "all_reduce",
                    "hook": args.hook,
+                   "workgroups_per_cu": args.workgroups_per_cu,
+                   "launch_lds_bytes": ddp.ddp_get_launch_lds(s.r),
                    "parallelism": "1 GPU, W replicas in HBM"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "bus_bw_GBps": round(bus, 2),

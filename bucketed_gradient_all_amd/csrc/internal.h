@@ -23,12 +23,17 @@ constexpr int unroll_for(int W)
 // The kernel uses no LDS; the launch reserves LDS only so that the hardware
 // dispatcher keeps at most this many workgroups on a CU. Fewer tiles in
 // flight keep each of the 2W streams' in-flight window narrow (a few MiB
-// across the chip), which measured 4-8% faster than full occupancy for
-// W >= 3; the reduce-scatter (one write stream) and U = 1 (smaller tiles)
-// do best at two per CU; W <= 2 (four streams) at full occupancy.
-constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter)
+// across the chip), which measured 2-8% faster than full occupancy for fp32
+// inputs and W >= 3; the reduce-scatter (one write stream) and U = 1
+// (smaller tiles) do best at two per CU; W <= 2 (four streams) and the
+// all-reduce of bf16 wgrads into fp32 main_grad at full occupancy.
+// bf16_accum: input mode DDP_IN_BF16_ACCUM_F32.
+constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum)
 {
-    return W <= 2 ? 0 : ((reduce_scatter || unroll_for(W) == 1) ? 2 : 1);
+    if (W <= 2) return 0;
+    if (reduce_scatter) return 2;
+    if (bf16_accum) return 0;
+    return unroll_for(W) == 1 ? 2 : 1;
 }
 
 // Elements one workgroup covers (one tile).

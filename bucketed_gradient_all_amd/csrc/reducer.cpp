@@ -219,7 +219,8 @@ struct ddp_reducer {
     // LDS each launch reserves so that at most k of its workgroups share a CU
     unsigned launch_lds() const
     {
-        const int k = workgroups_per_cu == 0 ? ddp::auto_workgroups_per_cu(pv.W, pv.reduce_scatter)
+        const int k = workgroups_per_cu == 0 ? ddp::auto_workgroups_per_cu(pv.W, pv.reduce_scatter,
+                                                                            pv.mode == DDP_IN_BF16_ACCUM_F32)
                                              : (workgroups_per_cu < 0 ? 0 : workgroups_per_cu);
         if (k <= 0 || lds_per_cu <= 0) return 0;
         int bytes = lds_per_cu / (k + 1) + 2048;   // k fit, k + 1 do not

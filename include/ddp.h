@@ -289,11 +289,13 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
  * LDS; a launch reserves LDS only so that the hardware dispatcher keeps at
  * most n of its workgroups on a CU. Fewer tiles in flight keep the 2W
  * streams' windows narrow, which suits HBM: on MI355X this measured 4-8%
- * faster than full occupancy for W >= 3 when the reduction has the GPU to
- * itself. The reserved LDS is unavailable to kernels that share the CUs, so
- * a caller whose backward kernels need that LDS may prefer no cap.
- *   n = 0  automatic (default): none for W <= 2, two per CU for
- *          reduce-scatter and for W >= 9, one per CU otherwise;
+ * faster than full occupancy for fp32 inputs and W >= 3. The reserved LDS is
+ * unavailable to kernels that share the CUs; with a GEMM backward running
+ * beside the reduction the cap still measured no worse, but a caller whose
+ * backward kernels need that LDS may prefer no cap.
+ *   n = 0  automatic (default): none for W <= 2 and for the all-reduce in
+ *          DDP_IN_BF16_ACCUM_F32 mode; two per CU for reduce-scatter and
+ *          for W >= 9; one per CU otherwise;
  *   n < 0  no cap (no LDS reserved; occupancy limited by registers only);
  *   1..8   at most n per CU.
  * Takes effect at the next launch; results do not depend on it.

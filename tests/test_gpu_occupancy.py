@@ -18,9 +18,10 @@ def _lds_per_cu():
     return v.value
 
 
-@pytest.mark.parametrize("W,collective", [(2, 0), (8, 0), (8, 1), (16, 0), (12, 0)])
-def test_results_do_not_depend_on_the_cap(W, collective):
-    wl = _small_workload(5100 + W + collective, W, 0)
+@pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (8, 0, 0), (8, 1, 0), (16, 0, 0), (12, 0, 0),
+                                               (16, 0, 2), (16, 1, 2)])
+def test_results_do_not_depend_on_the_cap(W, collective, mode):
+    wl = _small_workload(5100 + W + collective, W, mode)
     run = Run(wl, collective=collective)
     ddp = run.ddp
     L = _lds_per_cu()
@@ -28,10 +29,17 @@ def test_results_do_not_depend_on_the_cap(W, collective):
         ddp.ddp_set_workgroups_per_cu(run.r, n)
         lds = ddp.ddp_get_launch_lds(run.r)
         if n == 0:
-            k = 0 if W <= 2 else (2 if (collective or W > 8) else 1)
+            if W <= 2:
+                k = 0
+            elif collective:
+                k = 2
+            elif mode == 2:
+                k = 0
+            else:
+                k = 2 if W > 8 else 1
         else:
             k = max(n, 0)
-        say(f"case W={W} rs={collective} cap={n} lds={lds} (per CU {L})")
+        say(f"case W={W} rs={collective} mode={mode} cap={n} lds={lds} (per CU {L})")
         if k == 0:
             assert lds == 0
         else:
