@@ -442,3 +442,43 @@ def test_reduce_scatter_megatron_sampled_bit_exact():
         assert m.sum() > 0
         assert_bits(got, want[m], f"megatron rs replica {w}")
     run.close()
+
+
+# ------------------------------------------------------------ degenerate
+def test_empty_model_launches_nothing():
+    from synth.workloads import Workload, DIST_UNIFORM
+    wl = Workload("empty", [], world=4, cap_bytes=1024, first_cap_bytes=1024, dist=DIST_UNIFORM)
+    run = Run(wl)
+    ddp = run.ddp
+    assert run.plan.n_buckets == 0
+    ddp.ddp_set_timing(run.r, True)
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_mark_ready_many(run.r, [])
+    ddp.ddp_finish(run.r, host_blocking=True)
+    assert len(ddp.ddp_get_timings(run.r)[0]) == 0
+    with pytest.raises(ddp.DDPError):
+        ddp.ddp_mark_ready(run.r, 0)
+    run.close()
+
+
+def test_zero_size_gradients_only():
+    """Buckets that hold only zero-size gradients complete and launch no work."""
+    from synth.workloads import Workload, DIST_UNIFORM
+    wl = Workload("zeros", [(0,), (0,), (0,)], world=3, cap_bytes=0, first_cap_bytes=0, dist=DIST_UNIFORM)
+    run = Run(wl)
+    assert run.plan.n_buckets == 3 and run.total == 0
+    run.step()
+    assert run.ddp.ddp_get_launched(run.r) == 3
+    run.close()
+
+
+@pytest.mark.parametrize("W", [2, 32, 100])
+def test_one_element_many_replicas(W):
+    """One element, so every chunk but the first is empty; the fold starts at
+    replica 0."""
+    from synth.workloads import Workload, DIST_NORMAL
+    wl = Workload(f"one_w{W}", [(1,)], world=W, cap_bytes=0, first_cap_bytes=0, dist=DIST_NORMAL, sigma=1.0)
+    run = Run(wl)
+    run.step()
+    check_full(run)
+    run.close()
