@@ -69,7 +69,7 @@ def measured_traffic(workload: str):
 
 
 class Session:
-    def __init__(self, wl, arena: bool = False, stagger: int = 0, backward_kind: str = "spin"):
+    def __init__(self, wl, arena: bool = False, stagger=None, backward_kind: str = "spin"):
         import numpy as np
         import torch
 
@@ -85,7 +85,9 @@ class Session:
         self.total = sum(bb) // 4
         self.bucket_bytes = bb
         t0 = time.perf_counter()
-        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena, stagger=stagger)
+        from synth.device import REPLICA_STAGGER
+        self.stagger = REPLICA_STAGGER if stagger is None else stagger
+        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena, stagger=self.stagger)
         log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
         self.compute = torch.cuda.Stream()
         self.comm = torch.cuda.Stream()
@@ -348,8 +350,11 @@ def main():
     ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
     ap.add_argument("--hook", default="none", choices=list(HOOKS),
                     help="built-in communication hook: the fp32 mean, or bf16 / fp16 compression")
-    ap.add_argument("--stagger", type=int, default=0,
-                    help="bytes by which replica w's buffers start w * stagger into their allocations")
+    ap.add_argument("--arena", action="store_true",
+                    help="carve every replica buffer out of one allocation instead of one allocation per buffer")
+    ap.add_argument("--stagger", type=int, default=None,
+                    help="bytes by which replica w's buffers start w * stagger into their allocations "
+                         "(default: synth.device.REPLICA_STAGGER)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-ms", type=float, default=20.0,
@@ -413,7 +418,7 @@ def main():
         wl.name += f"_{args.hook}hook"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
-    s = Session(wl, stagger=args.stagger, backward_kind=args.backward_kind)
+    s = Session(wl, arena=args.arena, stagger=args.stagger, backward_kind=args.backward_kind)
     import bucketed_gradient_all_amd as ddp
     ddp.ddp_register_builtin_hook(s.r, hook)
     ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
@@ -511,6 +516,7 @@ def main():
                    "collective": "reduce_scatter" if wl.collective == wls.REDUCE_SCATTER else "all_reduce",
                    "hook": args.hook,
                    "workgroups_per_cu": args.workgroups_per_cu,
+                   "replica_stagger_bytes": s.stagger,
                    "launch_lds_bytes": ddp.ddp_get_launch_lds(s.r),
                    "parallelism": "1 GPU, W replicas in HBM"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),

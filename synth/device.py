@@ -21,13 +21,21 @@ from .workloads import (IN_BF16_ACCUM_F32, IN_F32_COPY, IN_F32_VIEW, STREAM_GRAD
                         Workload)
 
 ALIGN = 256
+
+# Placement of the simulated replicas. On W GPUs each replica's buffers live
+# in their own HBM; on one GPU, identical layouts in same-size allocations
+# would put element e of every replica at the same offset, so the 2W streams
+# hit correlated HBM channels at the same moment, a collision W GPUs do not
+# have. Replica w's buffers therefore start w * REPLICA_STAGGER bytes into
+# their allocations (a multiple of 256, so alignment is unchanged).
+REPLICA_STAGGER = 12288
 SENTINEL = -1   # 0xFFFFFFFF: a NaN pattern the reduction never produces from finite inputs
 
 
 class DeviceInputs:
     def __init__(self, wl: Workload, flat_offset_elems: Sequence[int], total_elems: int, device: str = "cuda",
                  seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0, arena: bool = False,
-                 stagger: int = 0):
+                 stagger: int = REPLICA_STAGGER):
         """misalign: bytes added to the start of every other gradient tensor
         (to exercise unaligned sources); flat_shift: elements the flat
         buffers start past their allocation, one value or one per replica (to
@@ -38,7 +46,7 @@ class DeviceInputs:
         flat buffers start w * stagger past their allocations, so that the W
         replicas' copies of one element do not sit at the same offset in
         same-size allocations (the HBM channel a line maps to depends on its
-        address)."""
+        address); see REPLICA_STAGGER."""
         import torch
 
         self.wl = wl
@@ -69,12 +77,12 @@ class DeviceInputs:
         self.flat_shift = shifts
         flat_bytes = (4 * (max(self.total, 1) + max(shifts)) + ALIGN - 1) // ALIGN * ALIGN
         if arena:
-            gb = self.grad_bytes if self.mode != IN_F32_VIEW else 0
+            gb = self.grad_bytes + (W - 1) * stagger if self.mode != IN_F32_VIEW else 0
             self._arena = torch.empty(W * (gb + flat_bytes), dtype=torch.uint8, device=device)
             base = 0
-            for _ in range(W):
+            for w in range(W):
                 if gb:
-                    self.grads.append(self._arena[base:base + gb])
+                    self.grads.append(self._arena[base + w * stagger:base + w * stagger + self.grad_bytes])
                     base += gb
             self._flat_alloc = []
             for _ in range(W):
