@@ -100,7 +100,7 @@ class Session:
         self.members = [np.asarray(m, np.int32) for m in self.plan.buckets()]
 
     def step(self, backward_us: float = 0.0, serial: bool = False, per_bucket: bool = False,
-             backward_only: bool = False):
+             backward_only: bool = False, scrub: bool = False):
         """per_bucket: one ready call per bucket, so each bucket is its own
         launch; otherwise all gradients are marked in one call and the
         buckets go out as one coalesced launch. backward_us > 0: a synthetic
@@ -112,6 +112,8 @@ class Session:
         bf16 GEMMs (backward_kind "gemm": they compete with the reduction
         for CUs and HBM, as a real backward would)."""
         ddp = self.ddp
+        if scrub:
+            self._scrub_mall()
         if backward_only:
             import synth
             tot = float(sum(self.bucket_bytes)) or 1.0
@@ -147,6 +149,18 @@ class Session:
         del self.inputs
         self.torch.cuda.synchronize()
         self.torch.cuda.empty_cache()
+
+    def _scrub_mall(self):
+        """Overwrite a 512 MiB buffer on the comm stream (twice the 256 MiB
+        MALL), so the next reduction starts with no bucket data cached; the
+        reduction's own timing events come after this in stream order."""
+        torch = self.torch
+        if getattr(self, "_scrub", None) is None:
+            self._scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+            self._scrub_val = 0.0
+        self._scrub_val += 1.0
+        with torch.cuda.stream(self.comm):
+            self._scrub.fill_(self._scrub_val)
 
     def _piece(self, us: float):
         """One piece of the synthetic backward on the compute stream."""
@@ -188,6 +202,13 @@ class Session:
         torch.cuda.synchronize()
         self.last_issue_s = issue / max(steps, 1)
         return time.perf_counter() - t0
+
+
+def bucket_alg_of(session, wl):
+    """Algorithmic bytes of each bucket's reduction."""
+    read = 6 if wl.input_mode == 2 else 4
+    per_elem = read * wl.world + 4 if wl.collective == 1 else (read + 4) * wl.world
+    return [per_elem * b // 4 for b in session.bucket_bytes]
 
 
 def cpu_baseline(wl, session, target_s: float, hook: int = 0):
@@ -350,6 +371,8 @@ def main():
     ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
     ap.add_argument("--hook", default="none", choices=list(HOOKS),
                     help="built-in communication hook: the fp32 mean, or bf16 / fp16 compression")
+    ap.add_argument("--no-scrub", action="store_true",
+                    help="skip the extra event-timed pass that overwrites a 512 MiB buffer before each step")
     ap.add_argument("--arena", action="store_true",
                     help="carve every replica buffer out of one allocation instead of one allocation per buffer")
     ap.add_argument("--stagger", type=int, default=None,
@@ -436,14 +459,22 @@ def main():
     ev_elapsed = s.timed(args.steps)
     first, count, ms = ddp.ddp_get_timings(s.r)
     ddp.ddp_set_timing(s.r, False)
+    # the same again with the MALL overwritten before every step (cold caches,
+    # as after a backward): reported beside the back-to-back figure
+    scrubbed = None
+    if not args.no_scrub:
+        ddp.ddp_set_timing(s.r, True)
+        s.timed(args.steps, scrub=True)
+        sf, sc_, sms = ddp.ddp_get_timings(s.r)
+        ddp.ddp_set_timing(s.r, False)
+        if sms.size:
+            scrubbed = (sum(sum(bucket_alg_of(s, wl)[f:f + c]) for f, c in zip(sf, sc_)), float(sms.sum()) / 1e3)
     log(f"[bench] step {elapsed / args.steps * 1e3:.3f} ms (host issue {issue_plain * 1e3:.3f} ms); "
         f"{ev_elapsed / args.steps * 1e3:.3f} ms with per-launch events")
     step_s = elapsed / args.steps
     value = bytes_per_step / step_s / 1e9
     W = wl.world
-    read = 6 if wl.input_mode == 2 else 4
-    per_elem = read * W + 4 if wl.collective == wls.REDUCE_SCATTER else (read + 4) * W
-    bucket_alg = [per_elem * b // 4 for b in s.bucket_bytes]
+    bucket_alg = bucket_alg_of(s, wl)
     launch_bytes = [sum(bucket_alg[f:f + c]) for f, c in zip(first, count)]
     kernel_s = float(ms.sum()) / 1e3
     launches = len(ms)
@@ -526,7 +557,9 @@ def main():
                      "kernel": "bucket_reduce (reduce_fixed)", "launches": launches,
                      "buckets_per_launch": round(float(count.mean()), 2) if launches else None,
                      "algorithmic_bytes_per_launch": int(per_launch_bytes),
-                     "avg_launch_us": round(kernel_s / max(launches, 1) * 1e6, 2)},
+                     "avg_launch_us": round(kernel_s / max(launches, 1) * 1e6, 2),
+                     "achieved_mall_scrubbed": (round(scrubbed[0] / scrubbed[1] / 1e9, 1)
+                                                if scrubbed is not None else None)},
     "per_bucket_launch": per_bucket_launch,
         "overlap": overlap,
         "cpu_baseline": cpu,
