@@ -465,10 +465,10 @@ def main():
     if not args.no_scrub:
         ddp.ddp_set_timing(s.r, True)
         s.timed(args.steps, scrub=True)
-        sf, sc_, sms = ddp.ddp_get_timings(s.r)
+        sfirst, scount, sms = ddp.ddp_get_timings(s.r)
         ddp.ddp_set_timing(s.r, False)
         if sms.size:
-            scrubbed = (sum(sum(bucket_alg_of(s, wl)[f:f + c]) for f, c in zip(sf, sc_)), float(sms.sum()) / 1e3)
+            scrubbed = (sum(sum(bucket_alg_of(s, wl)[f:f + c]) for f, c in zip(sfirst, scount)), float(sms.sum()) / 1e3)
     log(f"[bench] step {elapsed / args.steps * 1e3:.3f} ms (host issue {issue_plain * 1e3:.3f} ms); "
         f"{ev_elapsed / args.steps * 1e3:.3f} ms with per-launch events")
     step_s = elapsed / args.steps
@@ -527,7 +527,9 @@ def main():
         torch.cuda.synchronize()
         cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds, hook)
 
-    traffic = measured_traffic(wl.name)
+    # the committed counters describe the default launch and layout only
+    default_setup = args.workgroups_per_cu == 0 and args.stagger is None and not args.arena
+    traffic = measured_traffic(wl.name) if default_setup else None
     out = {
         "metric": METRIC,
         "value": round(value, 2),
