@@ -482,3 +482,56 @@ def test_one_element_many_replicas(W):
     run.step()
     check_full(run)
     run.close()
+
+
+def test_more_than_2pow31_elements():
+    """One tensor of 2^31 + 1000 elements (8 GiB per buffer), W = 2: element
+    indices beyond 32 bits in every kernel path; sampled against the oracle
+    at both ends, at the chunk boundary and at 2^31 itself."""
+    torch = _torch()
+    from synth.workloads import Workload, DIST_UNIFORM
+    from expect import expected_at, oracle_plan
+    n = (1 << 31) + 1000
+    wl = Workload("huge", [(n,)], world=2, cap_bytes=INF, first_cap_bytes=INF, dist=DIST_UNIFORM, seed=31)
+    say(f"case huge n={n}")
+    run = Run(wl)
+    run.step()
+    oplan = oracle_plan(wl)
+    q = -(-n // 2)
+    idx = sorted({0, 1, 3, 4, 63, 64, q - 5, q - 1, q, q + 1, q + 4, (1 << 31) - 1, 1 << 31, (1 << 31) + 1,
+                  n - 5, n - 4, n - 1} | set(int(x) for x in np.random.default_rng(0).integers(0, n, 64)))
+    flat_idx, want = expected_at(wl, oplan, [(0, i) for i in idx], wl.seed)
+    t = torch.from_numpy(np.asarray(flat_idx, np.int64)).cuda()
+    for w in range(2):
+        got = run.inputs.flat[w][:run.total].index_select(0, t).cpu().numpy()
+        assert_bits(got, want, f"huge replica {w}")
+    run.close()
+
+
+def test_two_reducers_interleaved_on_separate_streams():
+    """Two models' reducers in one process, each on its own stream pair,
+    with their marks interleaved: both bit-exact."""
+    torch = _torch()
+    from synth import workloads as wls
+    a = Run(wls.tiny())
+    b_wl = _small_workload(777, 8, 2)
+    b = Run(b_wl)
+    ddp = a.ddp
+    for it in range(3):
+        a.inputs.refill()
+        b.inputs.refill()
+        ddp.ddp_prepare_for_backward(a.r)
+        ddp.ddp_prepare_for_backward(b.r)
+        pa = list(range(len(a.wl.numel) - 1, -1, -1))
+        pb = list(range(len(b_wl.numel) - 1, -1, -1))
+        for i in range(max(len(pa), len(pb))):
+            if i < len(pa):
+                ddp.ddp_mark_ready(a.r, pa[i])
+            if i < len(pb):
+                ddp.ddp_mark_ready(b.r, pb[i])
+        ddp.ddp_finish(b.r, host_blocking=True)
+        ddp.ddp_finish(a.r, host_blocking=True)
+        check_full(a)
+        check_full(b)
+    a.close()
+    b.close()
