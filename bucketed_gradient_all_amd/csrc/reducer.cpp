@@ -687,9 +687,16 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
 int ddp_reducer_destroy(ddp_reducer *r)
 {
     if (!r) return DDP_OK;
+    // reductions still queued on the comm stream read and write the caller's
+    // buffers: wait for them, so the buffers may be freed once this returns
+    hipError_t e = hipSuccess;
+    if (r->device && r->ev_host) {
+        e = hipEventRecord(r->ev_host, r->comm);
+        if (e == hipSuccess) e = hipEventSynchronize(r->ev_host);
+    }
     destroy_events(r);
     delete r;
-    return DDP_OK;
+    return e == hipSuccess ? DDP_OK : hip_fail("waiting for outstanding reductions", e);
 }
 
 int ddp_prepare_for_backward(ddp_reducer *r)

@@ -158,7 +158,12 @@ size_t ddp_workspace_bytes(const ddp_reducer_desc *desc);
  * *out is set only on success. */
 int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out);
 
-/* Releases host state and events; the caller's buffers are untouched. NULL is a no-op. */
+/* Waits for every reduction the reducer queued on its comm stream, then
+ * releases host state, events and staging; the caller's buffers are
+ * untouched and may be freed once this returns. Reductions the caller queued
+ * on other streams through ddp_bucket_reduce are the caller's to wait for.
+ * NULL is a no-op. The reducer is released even when the wait reports an
+ * error (DDP_ERR_HIP). */
 int ddp_reducer_destroy(ddp_reducer *r);
 
 /* Resets every bucket's pending count and the per-iteration ready set before

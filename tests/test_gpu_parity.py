@@ -535,3 +535,24 @@ def test_two_reducers_interleaved_on_separate_streams():
         check_full(b)
     a.close()
     b.close()
+
+
+def test_destroy_waits_for_queued_reductions():
+    """A reduction queued behind 100 ms of compute-stream work is complete
+    when ddp_reducer_destroy returns, so the buffers may be freed."""
+    torch = _torch()
+    import synth
+    from synth import workloads as wls
+    run = Run(wls.tiny())
+    ddp = run.ddp
+    synth.spin_dev(100e3, run.compute.cuda_stream)
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_mark_ready_many(run.r, list(range(len(run.wl.numel) - 1, -1, -1)))
+    ddp.ddp_finish(run.r, host_blocking=False)
+    assert not run.comm.query()          # still waiting behind the compute stream
+    ddp.ddp_reducer_destroy(run.r)
+    assert run.comm.query()              # nothing of the reducer's left in flight
+    torch.cuda.synchronize()
+    check_full(run)
+    del run.inputs
+    torch.cuda.empty_cache()
