@@ -480,3 +480,89 @@ def test_workgroups_per_cu_rules():
         ddp.ddp_set_workgroups_per_cu(r, n)
         assert ddp.ddp_get_launch_lds(r) == 0      # no device: nothing to reserve
     ddp.ddp_reducer_destroy(r)
+
+
+def _call(fn, *a):
+    """Runs one call; returns (code, result)."""
+    try:
+        return 0, fn(*a)
+    except ddp.DDPError as e:
+        return e.code, getattr(e, "n_done", None)
+    except ModelError as e:
+        return e.code, None
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_random_api_sequences_match_the_oracle_model(seed):
+    """Random sequences of prepare, single and batched marks (repeats and bad
+    indices included), finish, bucket groups, no_sync and used tables: the
+    library and the oracle model agree on every status and every launch."""
+    rng = random.Random(1000 + seed)
+    W = rng.choice([1, 2, 3, 8])
+    P = rng.randint(1, 25)
+    numel = [rng.randint(0, 30) for _ in range(P)]
+    find_unused = rng.random() < 0.5
+    pb = [4 * n for n in numel]
+    plan = ddp.ddp_plan_buckets(pb, ddp.DDP_ORDER_REVERSE, rng.choice([0, 16, 64, 400]), rng.choice([16, 64]))
+    desc = ddp.Desc(W, numel, plan.bucket_of, plan.offset_in_bucket, plan.n_buckets, find_unused=find_unused)
+    r = ddp.ddp_reducer_create(desc)
+    log = []
+    ddp.ddp_register_comm_hook(r, lambda b: log.append(b) or 0)
+    model = ReducerModel(plan.buckets(), P, world=W, find_unused=find_unused)
+    B = plan.n_buckets
+    for step in range(120):
+        op = rng.choice(["prepare", "mark", "mark", "mark", "many", "finish", "groups", "sync", "used"])
+        before = len(log)
+        want = []
+        if op == "prepare":
+            c_code, _ = _call(ddp.ddp_prepare_for_backward, r)
+            m_code, _ = _call(model.prepare_for_backward)
+            if c_code == 0 and m_code == 0 and find_unused and rng.random() < 0.5:
+                used = [[int(rng.random() < 0.7) for _ in range(P)] for _ in range(W)]
+                assert _call(ddp.ddp_set_local_used, r, used)[0] == _call(model.set_local_used, used)[0]
+        elif op == "mark":
+            unready = [q for q in range(P) if not model.ready[q]]
+            p = rng.choice(unready) if unready and rng.random() < 0.8 else rng.randint(-1, P)
+            c_code, _ = _call(ddp.ddp_mark_ready, r, p)
+            m_code, got = _call(model.mark_ready, p)
+            want = got or []
+        elif op == "many":
+            unready = [q for q in range(P) if not model.ready[q]]
+            ps = [rng.randint(-1, P) if rng.random() < 0.1 or not unready else rng.choice(unready)
+                  for _ in range(rng.randint(1, 4))]
+            c_code, c_done = _call(ddp.ddp_mark_ready_many, r, ps)
+            m_code, m_done = 0, 0
+            for p in ps:
+                code, got = _call(model.mark_ready, p)
+                if code:
+                    m_code = code
+                    break
+                want += got
+                m_done += 1
+            if c_code:
+                assert c_done == m_done, (seed, step, ps)
+        elif op == "finish":
+            c_code, _ = _call(ddp.ddp_finish, r, 0)
+            m_code, got = _call(model.finish)
+            want = got or []
+        elif op == "groups":
+            if B > 1 and rng.random() < 0.8:
+                firsts = [0] + sorted(rng.sample(range(1, B), rng.randint(0, B - 1)))
+            elif rng.random() < 0.5:
+                firsts = []
+            else:
+                firsts = [rng.randint(-1, B)]
+            c_code, _ = _call(ddp.ddp_set_bucket_groups, r, firsts)
+            m_code, _ = _call(model.set_bucket_groups, firsts)
+        elif op == "sync":
+            flag = rng.random() < 0.7
+            c_code, _ = _call(ddp.ddp_set_require_sync, r, flag)
+            m_code, _ = _call(model.set_require_sync, flag)
+        else:
+            used = [[int(rng.random() < 0.7) for _ in range(P)] for _ in range(W)]
+            c_code, _ = _call(ddp.ddp_set_local_used, r, used)
+            m_code, _ = _call(model.set_local_used, used)
+        assert c_code == m_code, (seed, step, op, c_code, m_code)
+        assert log[before:] == want, (seed, step, op, log[before:], want)
+        assert ddp.ddp_get_launched(r) == model.next_bucket, (seed, step, op)
+    ddp.ddp_reducer_destroy(r)
