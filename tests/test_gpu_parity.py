@@ -33,7 +33,8 @@ def say(*a):
 class Run:
     """Device inputs + reducer for a workload, on two torch streams."""
 
-    def __init__(self, wl, misalign=0, flat_shift=0, seed=None, same_stream=False, collective=0):
+    def __init__(self, wl, misalign=0, flat_shift=0, seed=None, same_stream=False, collective=0,
+                 find_unused=False):
         torch = _torch()
         import bucketed_gradient_all_amd as ddp
         from synth.device import DeviceInputs
@@ -49,7 +50,7 @@ class Run:
         self.comm = self.compute if same_stream else torch.cuda.Stream()
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
                                   self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
-                                  collective=collective)
+                                  collective=collective, find_unused=find_unused)
         self.total = total
         self.bucket_flat = [int(x) // 4 for x in bucket_flat]
 
