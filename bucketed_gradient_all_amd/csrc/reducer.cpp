@@ -174,12 +174,15 @@ int validate(const ddp_reducer_desc *d, PlanView &pv)
         for (int32_t p : m) {
             if (pv.offset[p] != off)
                 return fail(DDP_ERR_INVALID, "bucket " + std::to_string(b) + ": gradients do not tile the bucket");
+            if (pv.numel[p] > (std::numeric_limits<int64_t>::max() - off) / 4)
+                return fail(DDP_ERR_INVALID, "bucket " + std::to_string(b) + " exceeds 2^63 bytes");
             off += 4 * pv.numel[p];
         }
+        if (off > std::numeric_limits<int64_t>::max() - running)
+            return fail(DDP_ERR_INVALID, "flat buffer exceeds 2^63 bytes");
         pv.bucket_bytes[b] = off;
         pv.bucket_flat[b] = running;
         running += off;
-        if (running < 0) return fail(DDP_ERR_INVALID, "flat buffer too large");
     }
     return DDP_OK;
 }
@@ -488,8 +491,13 @@ int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t
     if (!n_buckets) return fail(DDP_ERR_INVALID, "n_buckets is NULL");
     if (n_params < 0 || (n_params > 0 && !param_bytes)) return fail(DDP_ERR_INVALID, "bad gradient sizes");
     if (cap_bytes < 0 || first_cap_bytes < 0) return fail(DDP_ERR_INVALID, "caps must be non-negative");
-    for (int32_t p = 0; p < n_params; ++p)
+    int64_t total = 0;   // every bucket's bytes are at most the total: checked once here
+    for (int32_t p = 0; p < n_params; ++p) {
         if (param_bytes[p] < 0) return fail(DDP_ERR_INVALID, "gradient sizes must be non-negative");
+        if (param_bytes[p] > std::numeric_limits<int64_t>::max() - total)
+            return fail(DDP_ERR_INVALID, "gradient sizes add up to more than 2^63 bytes");
+        total += param_bytes[p];
+    }
 
     // the walk order [DDP-ch17 §17.3.1, §17.13; L15 §2.2]
     std::vector<int32_t> walk(n_params);

@@ -95,6 +95,12 @@ def test_plan_rejects_bad_arguments():
         ddp.ddp_plan_buckets([4, 4], 7, 8, 8)
     with pytest.raises(ddp.DDPError):
         ddp.ddp_plan_buckets([4, 4], ddp.DDP_ORDER_REVERSE, -1, 8)
+    big = (1 << 62) + 4
+    with pytest.raises(ddp.DDPError) as e:      # the sizes' sum does not fit int64
+        ddp.ddp_plan_buckets([big, big], ddp.DDP_ORDER_REVERSE, INF, INF)
+    assert e.value.code == ddp.DDP_ERR_INVALID and "2^63" in e.value.msg
+    p = ddp.ddp_plan_buckets([big, (1 << 62) - 8], ddp.DDP_ORDER_REVERSE, INF, INF)
+    assert list(p.bucket_bytes) == [(1 << 63) - 4]
 
 
 # ----------------------------------------------------------- state machine
@@ -238,6 +244,9 @@ def test_introspection():
         ddp.ddp_get_bucket(r, plan.n_buckets)
 
 
+M60 = (1 << 60) - 1      # the largest gradient a desc accepts, in elements
+
+
 def _desc(numel, bucket_of, offsets, nb, W=2, mode=ddp.DDP_IN_F32_COPY):
     return ddp.Desc(W, numel, bucket_of, offsets, nb, mode)
 
@@ -251,6 +260,8 @@ def _desc(numel, bucket_of, offsets, nb, W=2, mode=ddp.DDP_IN_F32_COPY):
     dict(numel=[-4, 4], bucket_of=[0, 0], offsets=[0, 0], nb=1),       # negative size
     dict(numel=[4], bucket_of=[0], offsets=[0], nb=1, W=0),            # no replicas
     dict(numel=[4], bucket_of=[0], offsets=[0], nb=1, mode=9),         # unknown mode
+    dict(numel=[M60] * 3, bucket_of=[0, 0, 0], offsets=[0, 4 * M60, 8 * M60], nb=1),  # bucket > 2^63 B
+    dict(numel=[M60] * 3, bucket_of=[0, 1, 2], offsets=[0, 0, 0], nb=3),               # flat > 2^63 B
 ])
 def test_invalid_descs_are_rejected(case):
     d = _desc(**case)
