@@ -181,9 +181,11 @@ class BucketPlan(NamedTuple):
 def ddp_plan_buckets(param_bytes: Sequence[int], order_mode: int = DDP_ORDER_REVERSE,
                      cap_bytes: int = 25 << 20, first_cap_bytes: int = 1 << 20,
                      order: Optional[Sequence[int]] = None) -> BucketPlan:
-    pb = np.ascontiguousarray(param_bytes, dtype=np.int64)
+    pb = np.ascontiguousarray(param_bytes, dtype=np.int64).reshape(-1)
     P = pb.size
-    od = np.ascontiguousarray(order if order is not None else [], dtype=np.int32)
+    od = np.ascontiguousarray(order if order is not None else [], dtype=np.int32).reshape(-1)
+    if order is not None and od.size != P:
+        raise ValueError(f"order must list all {P} gradients, got {od.size}")
     bucket_of = np.empty(P, np.int32)
     offset = np.empty(P, np.int64)
     bparams = np.empty(P, np.int32)
@@ -205,15 +207,24 @@ class Desc:
                  grads: Optional[Sequence[Sequence[int]]] = None, flat: Optional[Sequence[int]] = None,
                  workspace: int = 0, workspace_bytes: int = 0, compute_stream: int = 0, comm_stream: int = 0,
                  collective: int = DDP_ALL_REDUCE, find_unused: bool = False):
-        self.numel = np.ascontiguousarray(param_numel, dtype=np.int64)
-        self.bucket_of = np.ascontiguousarray(bucket_of, dtype=np.int32)
-        self.offset = np.ascontiguousarray(offset_in_bucket, dtype=np.int64)
+        self.numel = np.ascontiguousarray(param_numel, dtype=np.int64).reshape(-1)
+        self.bucket_of = np.ascontiguousarray(bucket_of, dtype=np.int32).reshape(-1)
+        self.offset = np.ascontiguousarray(offset_in_bucket, dtype=np.int64).reshape(-1)
         P = self.numel.size
+        if self.bucket_of.size != P or self.offset.size != P:
+            raise ValueError(f"bucket_of and offset_in_bucket need {P} entries, got "
+                             f"{self.bucket_of.size} and {self.offset.size}")
         self.grads = None
         if grads is not None:
-            self.grads = np.ascontiguousarray(np.asarray(grads, dtype=np.uint64).reshape(world * P)
-                                              if P else np.zeros(1, np.uint64))
-        self.flat = np.ascontiguousarray(flat, dtype=np.uint64) if flat is not None else None
+            g = np.asarray(grads, dtype=np.uint64).reshape(-1)
+            if g.size != world * P:
+                raise ValueError(f"grads needs {world}*{P} pointers, got {g.size}")
+            self.grads = np.ascontiguousarray(g if P else np.zeros(1, np.uint64))
+        self.flat = None
+        if flat is not None:
+            self.flat = np.ascontiguousarray(flat, dtype=np.uint64).reshape(-1)
+            if self.flat.size != world:
+                raise ValueError(f"flat needs {world} pointers, got {self.flat.size}")
         d = ddp_reducer_desc()
         d.world = world
         d.n_params = P
@@ -251,6 +262,15 @@ class Reducer:
         self.handle = handle
         self.desc = desc
         self._hook = None
+        self._hook_error: Optional[BaseException] = None
+
+    def check(self, rc: int) -> int:
+        """_check for calls that may run the Python hook: an exception the
+        hook raised becomes the cause of the DDPError."""
+        err, self._hook_error = self._hook_error, None
+        if rc < 0:
+            raise DDPError(rc, ddp_last_error()) from err
+        return rc
 
 
 def ddp_reducer_create(desc: Desc) -> Reducer:
@@ -270,7 +290,7 @@ def ddp_prepare_for_backward(r: Reducer) -> None:
 
 
 def ddp_mark_ready(r: Reducer, param: int) -> None:
-    _check(lib().ddp_mark_ready(r.handle, param))
+    r.check(lib().ddp_mark_ready(r.handle, param))
 
 
 def ddp_mark_ready_many(r: Reducer, params) -> int:
@@ -278,10 +298,11 @@ def ddp_mark_ready_many(r: Reducer, params) -> int:
     arr = np.ascontiguousarray(params, dtype=np.int32)
     done = ctypes.c_int32()
     rc = lib().ddp_mark_ready_many(r.handle, arr.ctypes.data, arr.size, ctypes.byref(done))
-    if rc < 0:
-        err = DDPError(rc, ddp_last_error())
+    try:
+        r.check(rc)
+    except DDPError as err:
         err.n_done = done.value
-        raise err
+        raise
     return done.value
 
 
@@ -303,16 +324,26 @@ def ddp_bucket_reduce(r: Reducer, bucket: int, stream: int) -> None:
 
 
 def ddp_finish(r: Reducer, host_blocking: bool = False) -> None:
-    _check(lib().ddp_finish(r.handle, 1 if host_blocking else 0))
+    r.check(lib().ddp_finish(r.handle, 1 if host_blocking else 0))
 
 
 def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> None:
-    """fn(bucket) -> int; None restores the default reduction."""
+    """fn(bucket) -> int (nonzero: failure); None restores the default
+    reduction. An exception fn raises fails the call that launched the
+    bucket, as a DDPError (DDP_ERR_HOOK) whose cause is that exception."""
     if fn is None:
         r._hook = None
         _check(lib().ddp_register_comm_hook(r.handle, HOOK_FN(), None))
         return
-    r._hook = HOOK_FN(lambda ctx, b: int(fn(b)))
+
+    def call(ctx, b):
+        try:
+            return int(fn(b))
+        except BaseException as e:   # ctypes would print it and return 0 (success)
+            r._hook_error = e
+            return -1
+
+    r._hook = HOOK_FN(call)
     _check(lib().ddp_register_comm_hook(r.handle, r._hook, None))
 
 

@@ -267,9 +267,17 @@ struct ddp_reducer {
     int32_t next = 0;
     int64_t marks = 0;
     bool finished = false;
+    // a launch of this backward failed (hook error or HIP error): buckets from
+    // failed_bucket on were not reduced and nothing more launches until reset
+    int32_t failed_bucket = -1;
+    int failed_code = DDP_OK;
+    std::string failed_msg;
 
     void reset()
     {
+        failed_bucket = -1;
+        failed_code = DDP_OK;
+        failed_msg.clear();
         masks_uploaded = false;
         pending.resize(pv.B);
         for (int b = 0; b < pv.B; ++b) pending[b] = int32_t(pv.members[b].size());
@@ -287,7 +295,16 @@ struct ddp_reducer {
             if (!ready[p]) out.push_back(p);
         return out;
     }
-    bool in_iteration() const { return sync && marks > 0 && !finished; }
+    // a synchronized backward has started and neither finished nor failed
+    bool in_iteration() const { return sync && marks > 0 && !finished && failed_bucket < 0; }
+
+    // the end of a synchronized backward: the next window of used tables starts empty
+    void end_window()
+    {
+        if (!pv.find_unused) return;
+        std::fill(window.begin(), window.end(), 0);
+        window_set = false;
+    }
 
     void set_groups(const int32_t *first, int32_t n)
     {
@@ -399,9 +416,10 @@ int upload_masks(ddp_reducer *r)
     return DDP_OK;
 }
 
-int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
+// Issues buckets [b0, b1); on failure *at is the first bucket not issued.
+int issue_buckets(ddp_reducer *r, int32_t b0, int32_t b1, int32_t *at)
 {
-    if (b0 >= b1) return DDP_OK;
+    *at = b0;
     if (r->device && r->compute != r->comm) {
         hipError_t e = hipStreamQuery(r->compute);
         if (e == hipErrorNotReady) {
@@ -414,6 +432,7 @@ int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
     if (urc != DDP_OK) return urc;
     if (r->hook) {
         for (int32_t b = b0; b < b1; ++b) {
+            *at = b;
             int rc = r->hook(r->hook_ctx, b);
             if (rc != 0) return fail(DDP_ERR_HOOK, "communication hook returned " + std::to_string(rc) +
                                                        " for bucket " + std::to_string(b));
@@ -422,6 +441,27 @@ int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
     }
     if (!r->device) return fail(DDP_ERR_INVALID, "no device buffers and no communication hook");
     return enqueue_reduce(r, b0, b1, r->comm);
+}
+
+// Launch of buckets [b0, b1), which r->next has already moved past. A failed
+// launch ends the backward's reductions: its error is returned here, every
+// later launch of the backward is refused with the same code, and ddp_finish
+// reports the buckets that were not reduced.
+int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
+{
+    if (b0 >= b1) return DDP_OK;
+    if (r->failed_bucket >= 0)
+        return fail(r->failed_code, "buckets " + std::to_string(b0) + ".." + std::to_string(b1 - 1) +
+                                        " not launched: the launch of bucket " + std::to_string(r->failed_bucket) +
+                                        " failed earlier in this backward");
+    int32_t at = b0;
+    const int rc = issue_buckets(r, b0, b1, &at);
+    if (rc != DDP_OK) {
+        r->failed_bucket = at;
+        r->failed_code = rc;
+        r->failed_msg = g_err;
+    }
+    return rc;
 }
 
 // One gradient-ready mark [DDP-ch17 §17.12]: advances r->next past every
@@ -714,6 +754,7 @@ int ddp_prepare_for_backward(ddp_reducer *r)
         return fail(DDP_ERR_UNFINISHED,
                     "the previous iteration's reduction never finished before a new one was prepared; "
                     "gradients never marked ready: " + list_params(r->unready()));
+    if (r->failed_bucket >= 0 && !r->finished) r->end_window();   // a failed backward never finished
     r->reset();
     r->sync = r->require_sync;
     return DDP_OK;
@@ -766,6 +807,13 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
         r->finished = true;
         return DDP_OK;
     }
+    if (r->failed_bucket >= 0) {
+        r->finished = true;
+        r->end_window();
+        return fail(r->failed_code, "buckets " + std::to_string(r->failed_bucket) + ".." +
+                                        std::to_string(r->pv.B - 1) + " of this backward were not reduced: " +
+                                        r->failed_msg);
+    }
     if (r->pv.find_unused && r->marks == 0 && r->next < r->pv.B) {
         // a backward in which no hook fired: every gradient unused everywhere
         // still completes, as at a first hook
@@ -796,10 +844,7 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
         if (e != hipSuccess) return hip_fail("finish", e);
     }
     r->finished = true;
-    if (r->pv.find_unused) {
-        std::fill(r->window.begin(), r->window.end(), 0);
-        r->window_set = false;
-    }
+    r->end_window();
     return DDP_OK;
 }
 

@@ -169,7 +169,9 @@ int ddp_reducer_destroy(ddp_reducer *r);
 /* Resets every bucket's pending count and the per-iteration ready set before
  * a backward [DDP-ch17 §17.12, §17.16]. DDP_ERR_UNFINISHED if gradients were
  * marked since the last reset but the iteration was never finished; the
- * message lists the gradients that got none, ascending [DDP-ch17 §17.6]. */
+ * message lists the gradients that got none, ascending [DDP-ch17 §17.6]. A
+ * backward in which a launch failed needs no ddp_finish: its error was
+ * already returned, and the reset discards its used tables. */
 int ddp_prepare_for_backward(ddp_reducer *r);
 
 /* The gradient-ready hook for gradient `param` [DDP-ch17 §17.3, §17.12; L15
@@ -184,7 +186,10 @@ int ddp_prepare_for_backward(ddp_reducer *r);
  * buckets on the comm stream. May launch 0..B buckets. Inside no_sync the
  * call only checks the index (see ddp_set_require_sync).
  * Errors: DDP_ERR_INVALID (index out of range), DDP_ERR_ALREADY_READY,
- * DDP_ERR_HIP, DDP_ERR_HOOK; a launch that failed still counts as issued. */
+ * DDP_ERR_HIP, DDP_ERR_HOOK (a launch failed; the mark itself counts). A
+ * failed launch ends the backward's reductions: the buckets from the one
+ * that failed on are not reduced, every later launch in the same backward is
+ * refused with the same code, and ddp_finish reports the failure. */
 int ddp_mark_ready(ddp_reducer *r, int32_t param);
 
 /* ddp_mark_ready for params[0], params[1], ... in that order, in one call
@@ -221,7 +226,10 @@ int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
 /* End of backward [DDP-ch17 §17.41; MegatronDDP §5]: checks that every bucket
  * launched (DDP_ERR_NOT_READY otherwise, listing the gradients not marked
  * ready), then makes the compute stream wait for the comm stream; with
- * host_blocking != 0 the host also waits for the reductions to complete. */
+ * host_blocking != 0 the host also waits for the reductions to complete.
+ * If a launch of this backward failed, it returns that launch's error code
+ * (DDP_ERR_HOOK or DDP_ERR_HIP), naming the buckets that were not reduced,
+ * and ends the backward. */
 int ddp_finish(ddp_reducer *r, int32_t host_blocking);
 
 /* no_sync [L15 §4.1; PTD-notes §2.2.4]: with sync == 0, the backward passes

@@ -195,6 +195,69 @@ def test_hook_error_and_missing_device():
     assert e.value.code == ddp.DDP_ERR_INVALID
 
 
+def test_hook_exception_fails_the_launching_call():
+    r, plan, log = host_reducer([4, 4, 4], 16, 16)     # one gradient per bucket
+
+    def hook(b):
+        if b == 1:
+            raise KeyError("bucket 1")
+        return 0
+
+    ddp.ddp_register_comm_hook(r, hook)
+    calls = []
+    inner = hook
+    ddp.ddp_register_comm_hook(r, lambda b: calls.append(b) or inner(b))
+    ddp.ddp_mark_ready(r, 2)                            # bucket 0: fine
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready_many(r, [1, 0])              # buckets 1 and 2: 1 fails, 2 is not tried
+    assert e.value.code == ddp.DDP_ERR_HOOK and isinstance(e.value.__cause__, KeyError)
+    assert e.value.n_done == 2
+    assert calls == [0, 1]
+    with pytest.raises(ddp.DDPError) as e:              # finish reports the buckets not reduced
+        ddp.ddp_finish(r)
+    assert e.value.code == ddp.DDP_ERR_HOOK and "buckets 1..2" in e.value.msg
+    assert e.value.__cause__ is None
+    # the next backward starts afresh and reduces every bucket
+    ddp.ddp_register_comm_hook(r, lambda b: calls.append(b) or 0)
+    ddp.ddp_prepare_for_backward(r)
+    ddp.ddp_mark_ready_many(r, [2, 1, 0])
+    ddp.ddp_finish(r)
+    assert calls == [0, 1, 0, 1, 2]
+
+
+def test_no_launch_after_a_failed_launch():
+    """Later buckets of the same backward are refused, not launched out of
+    order; a prepare without finish after the failure is allowed."""
+    r, plan, log = host_reducer([4] * 4, 16, 16)        # buckets [[3], [2], [1], [0]]
+    calls = []
+    ddp.ddp_register_comm_hook(r, lambda b: calls.append(b) or (3 if b == 1 else 0))
+    ddp.ddp_mark_ready(r, 3)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, 2)
+    assert e.value.code == ddp.DDP_ERR_HOOK and "returned 3 for bucket 1" in e.value.msg
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, 1)
+    assert e.value.code == ddp.DDP_ERR_HOOK and "bucket 1 failed earlier" in e.value.msg
+    assert calls == [0, 1]
+    assert ddp.ddp_get_ready_order(r) == [3, 2, 1]      # the marks themselves counted
+    ddp.ddp_prepare_for_backward(r)
+    ddp.ddp_register_comm_hook(r, lambda b: calls.append(b) or 0)
+    ddp.ddp_mark_ready_many(r, [3, 2, 1, 0])
+    ddp.ddp_finish(r)
+    assert calls == [0, 1, 0, 1, 2, 3]
+
+
+def test_binding_checks_array_lengths():
+    with pytest.raises(ValueError):
+        ddp.ddp_plan_buckets([4, 4, 4], ddp.DDP_ORDER_GIVEN, 8, 8, order=[0, 1])
+    with pytest.raises(ValueError):
+        ddp.Desc(2, [4, 4], [0], [0, 16], 1)
+    with pytest.raises(ValueError):
+        ddp.Desc(2, [4, 4], [0, 0], [0, 16], 1, grads=[[1, 2]], flat=[3, 4])
+    with pytest.raises(ValueError):
+        ddp.Desc(2, [4, 4], [0, 0], [0, 16], 1, grads=[[1, 2], [5, 6]], flat=[3])
+
+
 def test_explicit_reduce_of_unready_bucket_is_refused():
     r, plan, log = host_reducer([2, 2, 2, 2], 16, 16)   # 8-byte gradients: buckets [[3,2],[1,0]]
     assert plan.buckets() == [[3, 2], [1, 0]]
