@@ -45,6 +45,7 @@ def host_cores() -> int:
 
 HOOKS = {"none": 0, "bf16": 1, "fp16": 2}          # DDP_HOOK_ALLREDUCE, _BF16_COMPRESS, _FP16_COMPRESS
 HOOK_FORMATS = {1: "bf16", 2: "fp16"}
+FIXED_WORLDS = (1, 2, 3, 4, 5, 6, 7, 8, 16, 32)   # replica counts with a compile-time kernel instance
 
 
 def kernel_source_hash() -> str:
@@ -68,8 +69,21 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def unused_table(wl, frac: float, global_frac: float, seed: int = 2024):
+    """Seeded used table [W][P] (1 = used) for unused-parameter detection:
+    every (replica, gradient) pair is unused with probability frac, and every
+    gradient is unused on all replicas with probability global_frac (a branch
+    no replica took). Fixed across steps."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    P = len(wl.numel)
+    used = (rng.random((wl.world, P)) >= frac).astype(np.uint8)
+    used[:, rng.random(P) < global_frac] = 0
+    return used
+
+
 class Session:
-    def __init__(self, wl, arena: bool = False, stagger=None, backward_kind: str = "spin"):
+    def __init__(self, wl, arena: bool = False, stagger=None, backward_kind: str = "spin", used=None):
         import numpy as np
         import torch
 
@@ -91,13 +105,17 @@ class Session:
         log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
         self.compute = torch.cuda.Stream()
         self.comm = torch.cuda.Stream()
+        self.used = used
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
                                   self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
-                                  collective=wl.collective)
-        self.order = np.arange(len(wl.numel) - 1, -1, -1, dtype=np.int32)
+                                  collective=wl.collective, find_unused=used is not None)
+        # gradients no replica used are marked ready by the library at the
+        # backward's first mark; the backward marks only the others
+        marked = np.ones(len(wl.numel), bool) if used is None else used.any(axis=0)
+        self.order = np.array([p for p in range(len(wl.numel) - 1, -1, -1) if marked[p]], dtype=np.int32)
         self.backward_kind = backward_kind
         self._gemm = None
-        self.members = [np.asarray(m, np.int32) for m in self.plan.buckets()]
+        self.members = [np.asarray([p for p in m if marked[p]], np.int32) for m in self.plan.buckets()]
 
     def step(self, backward_us: float = 0.0, serial: bool = False, per_bucket: bool = False,
              backward_only: bool = False, scrub: bool = False):
@@ -121,6 +139,8 @@ class Session:
                 self._piece(backward_us * self.bucket_bytes[b] / tot)
             return
         ddp.ddp_prepare_for_backward(self.r)
+        if self.used is not None:
+            ddp.ddp_set_local_used(self.r, self.used)
         if backward_us <= 0 and not per_bucket:
             ddp.ddp_mark_ready_many(self.r, self.order)
         elif backward_us <= 0:
@@ -205,13 +225,24 @@ class Session:
 
 
 def bucket_alg_of(session, wl):
-    """Algorithmic bytes of each bucket's reduction."""
+    """Algorithmic bytes of each bucket's reduction: per element, 4 bytes (6
+    in the bf16 mode) read from every replica that used the gradient, and 4
+    written to every replica (to the chunk's owner only, for reduce-scatter)
+    unless no replica used it."""
+    import numpy as np
     read = 6 if wl.input_mode == 2 else 4
-    per_elem = read * wl.world + 4 if wl.collective == 1 else (read + 4) * wl.world
-    return [per_elem * b // 4 for b in session.bucket_bytes]
+    write = 4 if wl.collective == 1 else 4 * wl.world
+    if session.used is None:
+        return [(read * wl.world + write) * b // 4 for b in session.bucket_bytes]
+    users = session.used.sum(axis=0).astype(np.int64)
+    per_param = [int(n) * (read * int(u) + (write if u else 0)) for n, u in zip(wl.numel, users)]
+    out = [0] * len(session.bucket_bytes)
+    for p, b in enumerate(session.plan.bucket_of):
+        out[int(b)] += per_param[p]
+    return out
 
 
-def cpu_baseline(wl, session, target_s: float, hook: int = 0):
+def cpu_baseline(wl, session, target_s: float, hook: int = 0, used=None):
     """The oracle (threaded fold, as written) on the first buckets of the
     same workload, inputs regenerated on the host; only the fold is timed.
     With a compression hook the oracle is the single-threaded numpy one."""
@@ -243,6 +274,11 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0):
             g = np.empty(n, np.uint16) if wl.input_mode == IN_BF16_ACCUM_F32 else None
             for p in oplan.buckets[b]:
                 o, m = oplan.offset_in_bucket[p] // 4, wl.numel[p]
+                if used is not None and not used[w][p]:   # a replica's unused slice is zero-filled
+                    x[o:o + m] = 0.0
+                    if g is not None:
+                        g[o:o + m] = 0
+                    continue
                 if wl.input_mode == IN_BF16_ACCUM_F32:
                     x[o:o + m] = synth.host_f32(synth.key(wl.seed, STREAM_MAIN, w, p), wl.dist, sc, m)
                     g[o:o + m] = synth.host_bf16(synth.key(wl.seed, STREAM_WGRAD, w, p), wl.dist, sc, m)
@@ -284,7 +320,13 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0):
         for b, out in zip(chosen, outs):
             lo = sum(oplan.bucket_bytes[:b]) // 4
             got = session.inputs.flat[0][lo:lo + out.size].cpu().numpy()
-            match &= bool(np.array_equal(got.view(np.uint32), out.view(np.uint32)))
+            written = np.ones(out.size, bool)
+            if used is not None:      # gradients no replica used keep their contents
+                for p in oplan.buckets[b]:
+                    if not any(used[w][p] for w in range(wl.world)):
+                        o = oplan.offset_in_bucket[p] // 4
+                        written[o:o + wl.numel[p]] = False
+            match &= bool(np.array_equal(got.view(np.uint32)[written], out.view(np.uint32)[written]))
     n_elems = sum(oplan.bucket_bytes[b] for b in chosen) // 4
     return {
         "value": round(gbps_mt, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -371,6 +413,11 @@ def main():
     ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
     ap.add_argument("--hook", default="none", choices=list(HOOKS),
                     help="built-in communication hook: the fp32 mean, or bf16 / fp16 compression")
+    ap.add_argument("--unused-frac", type=float, default=0.0,
+                    help="unused-parameter detection: each (replica, gradient) pair unused with this "
+                         "probability (seeded; 0 with --unused-global-frac 0: detection off)")
+    ap.add_argument("--unused-global-frac", type=float, default=0.0,
+                    help="unused-parameter detection: each gradient unused on every replica with this probability")
     ap.add_argument("--no-scrub", action="store_true",
                     help="skip the extra event-timed pass that overwrites a 512 MiB buffer before each step")
     ap.add_argument("--arena", action="store_true",
@@ -439,13 +486,17 @@ def main():
     hook = HOOKS[args.hook]
     if hook:
         wl.name += f"_{args.hook}hook"
+    used = None
+    if args.unused_frac > 0 or args.unused_global_frac > 0:
+        used = unused_table(wl, args.unused_frac, args.unused_global_frac)
+        wl.name += f"_unused{args.unused_frac:g}_{args.unused_global_frac:g}"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
-    s = Session(wl, arena=args.arena, stagger=args.stagger, backward_kind=args.backward_kind)
+    s = Session(wl, arena=args.arena, stagger=args.stagger, backward_kind=args.backward_kind, used=used)
     import bucketed_gradient_all_amd as ddp
     ddp.ddp_register_builtin_hook(s.r, hook)
     ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
-    bytes_per_step = wl.algorithmic_bytes()
+    bytes_per_step = sum(bucket_alg_of(s, wl))
 
     for _ in range(args.warmup):
         s.step()
@@ -525,7 +576,7 @@ def main():
         s.inputs.refill()
         s.step()
         torch.cuda.synchronize()
-        cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds, hook)
+        cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds, hook, used)
 
     # the committed counters describe the default launch and layout only
     default_setup = args.workgroups_per_cu == 0 and args.stagger is None and not args.arena
@@ -548,6 +599,10 @@ def main():
                    "input_mode": MODE_NAMES[wl.input_mode], "bytes_per_step": bytes_per_step,
                    "collective": "reduce_scatter" if wl.collective == wls.REDUCE_SCATTER else "all_reduce",
                    "hook": args.hook,
+                   "unused": None if used is None else {
+                       "pair_frac": args.unused_frac, "global_frac": args.unused_global_frac,
+                       "unused_pairs": int((used == 0).sum()),
+                       "gradients_unused_everywhere": int((~used.any(axis=0)).sum())},
                    "workgroups_per_cu": args.workgroups_per_cu,
                    "replica_stagger_bytes": s.stagger,
                    "launch_lds_bytes": ddp.ddp_get_launch_lds(s.r),
@@ -556,13 +611,14 @@ def main():
         "bus_bw_GBps": round(bus, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "bucket_reduce (reduce_fixed)", "launches": launches,
+                     "kernel": "bucket_reduce (reduce_fixed)" if W in FIXED_WORLDS else "bucket_reduce (reduce_generic)",
+                     "launches": launches,
                      "buckets_per_launch": round(float(count.mean()), 2) if launches else None,
                      "algorithmic_bytes_per_launch": int(per_launch_bytes),
                      "avg_launch_us": round(kernel_s / max(launches, 1) * 1e6, 2),
                      "achieved_mall_scrubbed": (round(scrubbed[0] / scrubbed[1] / 1e9, 1)
                                                 if scrubbed is not None else None)},
-    "per_bucket_launch": per_bucket_launch,
+        "per_bucket_launch": per_bucket_launch,
         "overlap": overlap,
         "cpu_baseline": cpu,
     }

@@ -1,0 +1,72 @@
+"""Host-side pieces of bench.py: the algorithmic byte count the roofline
+divides by, with and without unused-parameter masks, and the --gpus guard."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import bucketed_gradient_all_amd as ddp  # noqa: E402
+from synth import workloads as wls  # noqa: E402
+
+
+class _Session:
+    def __init__(self, wl, used=None):
+        self.plan = ddp.ddp_plan_buckets(wl.param_bytes, wl.order_mode, wl.cap_bytes, wl.first_cap_bytes)
+        self.bucket_bytes = [int(x) for x in self.plan.bucket_bytes]
+        self.used = used
+
+
+@pytest.mark.parametrize("name", ["tiny", "resnet50", "megatron_llama1b"])
+@pytest.mark.parametrize("collective", [0, 1])
+def test_bucket_bytes_add_up_to_the_workload(name, collective):
+    wl = wls.by_name(name)
+    wl.collective = collective
+    s = _Session(wl)
+    assert sum(bench.bucket_alg_of(s, wl)) == wl.algorithmic_bytes()
+    s.used = np.ones((wl.world, len(wl.numel)), np.uint8)
+    assert sum(bench.bucket_alg_of(s, wl)) == wl.algorithmic_bytes()
+
+
+def test_unused_bytes_counted_per_gradient():
+    """tiny (W=4, fp32 copy): a gradient used by u replicas moves 4u bytes
+    read + 16 written per element (4 for reduce-scatter), or nothing if u = 0."""
+    wl = wls.tiny()
+    P = len(wl.numel)
+    used = np.ones((4, P), np.uint8)
+    used[:, 0] = 0              # nobody
+    used[1:, 1] = 0             # only replica 0
+    used[3, 2] = 0              # three replicas
+    s = _Session(wl, used)
+    full = (4 * 4 + 16)
+    want = [full * n for n in wl.numel]
+    want[0] = 0
+    want[1] = (4 + 16) * wl.numel[1]
+    want[2] = (12 + 16) * wl.numel[2]
+    got = bench.bucket_alg_of(s, wl)
+    per_bucket = [sum(want[p] for p in m) for m in s.plan.buckets()]
+    assert got == per_bucket
+    wl.collective = 1
+    want_rs = [(4 * int(used[:, p].sum()) + (4 if used[:, p].any() else 0)) * n for p, n in enumerate(wl.numel)]
+    assert bench.bucket_alg_of(s, wl) == [sum(want_rs[p] for p in m) for m in s.plan.buckets()]
+
+
+def test_unused_table_is_seeded_and_has_the_requested_structure():
+    wl = wls.resnet50()
+    a = bench.unused_table(wl, 0.2, 0.05)
+    b = bench.unused_table(wl, 0.2, 0.05)
+    assert np.array_equal(a, b) and a.shape == (wl.world, len(wl.numel))
+    assert 0.15 < (a == 0).mean() < 0.3
+    assert (~a.any(axis=0)).sum() >= 1
+    assert bench.unused_table(wl, 0.0, 0.0).all()
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
