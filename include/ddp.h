@@ -331,7 +331,10 @@ int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched);
 /* Per-launch timing: while enabled, each default reduction launch (one
  * bucket, or a coalesced group) is bracketed by two HIP events on the stream
  * it runs on (timing-only events, without the system-scope fence). Enabling
- * (again) starts a new record list; the events are kept and reused.
+ * (again) starts a new record list; the events are kept and reused. The
+ * list, and the event pool with it, grows by one record (two events) per
+ * launch for as long as timing stays enabled; the pool is freed by
+ * ddp_reducer_destroy.
  * ddp_get_timings copies up to `capacity` records (launch order) of the
  * launches since timing was last enabled: the first bucket, the number of
  * buckets the launch covered, and the kernel's duration in ms. The caller
