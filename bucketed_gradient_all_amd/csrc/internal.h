@@ -11,12 +11,18 @@ namespace ddp {
 
 constexpr int kThreads = 256;   // one workgroup = four wave64s
 
-// Vector groups (of 4 elements) each thread carries per replica. More groups
-// give more loads in flight per wave; W groups' worth of registers are held
-// per unit, so the count shrinks as W grows.
-constexpr int unroll_for(int W)
+// Vector groups (of 4 elements) each thread carries per replica: the tile is
+// kThreads * 4 * U elements and a thread holds W * U 16-byte loads in flight.
+// Chosen by measurement together with the workgroups per CU below. For the
+// all-reduce (W read and W write streams), small tiles with two workgroups per
+// CU beat large tiles with one from W = 5 up (one workgroup's stores overlap
+// the other's loads), and W = 2 runs small tiles uncapped; W = 1, 3 and 4
+// keep four groups. The reduce-scatter (W reads, one write) keeps the larger
+// tiles up to W = 8.
+constexpr int unroll_for(int W, bool reduce_scatter)
 {
-    return W <= 4 ? 4 : (W <= 8 ? 2 : 1);
+    if (reduce_scatter) return W <= 4 ? 4 : (W <= 8 ? 2 : 1);
+    return (W == 2 || W >= 5) ? 1 : 4;
 }
 
 // Workgroups of one launch resident per CU (0: as many as registers allow).
@@ -33,13 +39,13 @@ constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum
     if (W <= 2) return 0;
     if (reduce_scatter) return 2;
     if (bf16_accum) return 0;
-    return unroll_for(W) == 1 ? 2 : 1;
+    return unroll_for(W, false) == 1 ? 2 : 1;
 }
 
 // Elements one workgroup covers (one tile).
-constexpr int64_t tile_elems(int W)
+constexpr int64_t tile_elems(int W, bool reduce_scatter)
 {
-    return int64_t(kThreads) * 4 * unroll_for(W);
+    return int64_t(kThreads) * 4 * unroll_for(W, reduce_scatter);
 }
 
 // A run of bucket elements that lies inside one gradient tensor and one ring

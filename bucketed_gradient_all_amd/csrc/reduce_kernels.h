@@ -252,13 +252,13 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // then all stores. CHECK = true: the segment's last tile, with per-lane
 // bounds; out-of-range lanes load the segment's first vector (in bounds, value
 // unused) and skip their stores.
-template <int W, int NOUT, int MODE, int HOOK, bool CHECK, bool USED>
+template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED>
 __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
                                             float *const (&ds)[NOUT], const bool (&on)[W], const DeviceSeg &sg,
                                             int64_t tin, const Scale &sc)
 {
-    constexpr int U = unroll_for(W);
-    constexpr int64_t TILE = tile_elems(W);
+    constexpr int U = unroll_for(W, RS);
+    constexpr int64_t TILE = tile_elems(W, RS);
     const int tid = int(threadIdx.x);
     int64_t e[U], el[U];
     bool ok[U];
@@ -313,7 +313,7 @@ template <int W, int MODE, int HOOK, bool RS, bool USED>
 __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, Scale sc)
 {
     constexpr int NOUT = RS ? 1 : W;
-    constexpr int64_t TILE = tile_elems(W);
+    constexpr int64_t TILE = tile_elems(W, RS);
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);
@@ -349,9 +349,9 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
     const int tid = int(threadIdx.x);
     if (sg.head >= 0) {
         if (sg.head + (tin + 1) * TILE <= sg.len)
-            vector_tile<W, NOUT, MODE, HOOK, false, USED>(xs, gs, ds, on, sg, tin, sc);
+            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED>(xs, gs, ds, on, sg, tin, sc);
         else if (sg.len - sg.head >= 4)
-            vector_tile<W, NOUT, MODE, HOOK, true, USED>(xs, gs, ds, on, sg, tin, sc);
+            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED>(xs, gs, ds, on, sg, tin, sc);
         if (tin == 0) {
             const int64_t body = (sg.len - sg.head) / 4 * 4;
             const int64_t tail = sg.len - sg.head - body;
@@ -372,7 +372,7 @@ template <int MODE, int HOOK>
 __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32_t tile_begin, Scale sc, int W,
                                                            int rs)
 {
-    const int64_t TILE = tile_elems(W);
+    const int64_t TILE = tile_elems(W, rs != 0);
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);

@@ -76,7 +76,7 @@ struct PlanView {
 // chunk of bucket element e is e / q with q = ceil(n / W) [DDP-ch17 §17.4].
 int build_segments(PlanView &pv, bool split_by_param)
 {
-    const int64_t TILE = ddp::tile_elems(pv.W);
+    const int64_t TILE = ddp::tile_elems(pv.W, pv.reduce_scatter);
     pv.segs.clear();
     pv.tile_seg.clear();
     pv.tile_begin.assign(pv.B, 0);

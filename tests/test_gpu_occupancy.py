@@ -18,8 +18,8 @@ def _lds_per_cu():
     return v.value
 
 
-@pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (8, 0, 0), (8, 1, 0), (16, 0, 0), (12, 0, 0),
-                                               (16, 0, 2), (16, 1, 2)])
+@pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (4, 0, 0), (6, 0, 1), (8, 0, 0), (8, 1, 0), (16, 0, 0),
+                                               (12, 0, 0), (16, 0, 2), (16, 1, 2)])
 def test_results_do_not_depend_on_the_cap(W, collective, mode):
     wl = _small_workload(5100 + W + collective, W, mode)
     run = Run(wl, collective=collective)
@@ -36,7 +36,7 @@ def test_results_do_not_depend_on_the_cap(W, collective, mode):
             elif mode == 2:
                 k = 0
             else:
-                k = 2 if W > 8 else 1
+                k = 2 if W >= 5 else 1      # small tiles, two per CU, from W = 5 up
         else:
             k = max(n, 0)
         say(f"case W={W} rs={collective} mode={mode} cap={n} lds={lds} (per CU {L})")
