@@ -13,7 +13,8 @@ constexpr int kThreads = 256;   // one workgroup = four wave64s
 
 // Vector groups (of 4 elements) each thread carries per replica: the tile is
 // kThreads * 4 * U elements and a thread holds W * U 16-byte loads in flight.
-// Chosen by measurement together with the workgroups per CU below. For the
+// Chosen by measurement together with the workgroups per CU each launch
+// allows (the host's occupancy rule). For the
 // all-reduce (W read and W write streams), small tiles with two workgroups per
 // CU beat large tiles with one from W = 5 up (one workgroup's stores overlap
 // the other's loads), and W = 2 runs small tiles uncapped; W = 1, 3 and 4
@@ -23,23 +24,6 @@ constexpr int unroll_for(int W, bool reduce_scatter)
 {
     if (reduce_scatter) return W <= 4 ? 4 : (W <= 8 ? 2 : 1);
     return (W == 2 || W >= 5) ? 1 : 4;
-}
-
-// Workgroups of one launch resident per CU (0: as many as registers allow).
-// The kernel uses no LDS; the launch reserves LDS only so that the hardware
-// dispatcher keeps at most this many workgroups on a CU. Fewer tiles in
-// flight keep each of the 2W streams' in-flight window narrow (a few MiB
-// across the chip), which measured 2-8% faster than full occupancy for fp32
-// inputs and W >= 3; the reduce-scatter (one write stream) and U = 1
-// (smaller tiles) do best at two per CU; W <= 2 (four streams) and the
-// all-reduce of bf16 wgrads into fp32 main_grad at full occupancy.
-// bf16_accum: input mode DDP_IN_BF16_ACCUM_F32.
-constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum)
-{
-    if (W <= 2) return 0;
-    if (reduce_scatter) return 2;
-    if (bf16_accum) return 0;
-    return unroll_for(W, false) == 1 ? 2 : 1;
 }
 
 // Elements one workgroup covers (one tile).
@@ -90,7 +74,7 @@ struct Scale {
 //   launch_bf16_hook:  through the bf16 compression hook
 //   launch_fp16_hook:  through the fp16 compression hook
 // lds_bytes: LDS each workgroup reserves (unused by the kernel; it bounds the
-// workgroups resident per CU, see auto_workgroups_per_cu).
+// workgroups resident per CU).
 hipError_t launch_mean(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
                        int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
 hipError_t launch_bf16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,

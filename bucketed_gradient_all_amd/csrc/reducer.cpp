@@ -49,6 +49,24 @@ std::string list_params(const std::vector<int32_t> &ps)
     return s;
 }
 
+// Workgroups of one launch resident per CU (0: as many as registers allow).
+// The kernel uses no LDS; the launch reserves LDS only so that the hardware
+// dispatcher keeps at most this many workgroups on a CU. Fewer tiles in
+// flight keep each of the 2W streams' in-flight window narrow (a few MiB
+// across the chip), which measured 2-8% faster than full occupancy for
+// W >= 3: one per CU with the large tiles (U = 4), two with the small ones
+// (U = 1, either input mode) and for the reduce-scatter. W <= 2 (four
+// streams), and the all-reduce of bf16 wgrads into fp32 main_grad with large
+// tiles (W = 3, 4: never measured capped), run at full occupancy.
+// bf16_accum: input mode DDP_IN_BF16_ACCUM_F32.
+constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum)
+{
+    if (W <= 2) return 0;
+    if (reduce_scatter) return 2;
+    if (ddp::unroll_for(W, false) == 1) return 2;
+    return bf16_accum ? 0 : 1;
+}
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x)
@@ -222,8 +240,8 @@ struct ddp_reducer {
     // LDS each launch reserves so that at most k of its workgroups share a CU
     unsigned launch_lds() const
     {
-        const int k = workgroups_per_cu == 0 ? ddp::auto_workgroups_per_cu(pv.W, pv.reduce_scatter,
-                                                                            pv.mode == DDP_IN_BF16_ACCUM_F32)
+        const int k = workgroups_per_cu == 0 ? auto_workgroups_per_cu(pv.W, pv.reduce_scatter,
+                                                                       pv.mode == DDP_IN_BF16_ACCUM_F32)
                                              : (workgroups_per_cu < 0 ? 0 : workgroups_per_cu);
         if (k <= 0 || lds_per_cu <= 0) return 0;
         int bytes = lds_per_cu / (k + 1) + 2048;   // k fit, k + 1 do not

@@ -18,8 +18,8 @@ def _lds_per_cu():
     return v.value
 
 
-@pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (4, 0, 0), (6, 0, 1), (8, 0, 0), (8, 1, 0), (16, 0, 0),
-                                               (12, 0, 0), (16, 0, 2), (16, 1, 2)])
+@pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (4, 0, 0), (4, 0, 2), (6, 0, 1), (8, 0, 0), (8, 1, 0),
+                                               (8, 0, 2), (16, 0, 0), (12, 0, 0), (16, 0, 2), (16, 1, 2)])
 def test_results_do_not_depend_on_the_cap(W, collective, mode):
     wl = _small_workload(5100 + W + collective, W, mode)
     run = Run(wl, collective=collective)
@@ -31,12 +31,10 @@ def test_results_do_not_depend_on_the_cap(W, collective, mode):
         if n == 0:
             if W <= 2:
                 k = 0
-            elif collective:
-                k = 2
-            elif mode == 2:
-                k = 0
+            elif collective or W >= 5:
+                k = 2                       # reduce-scatter; small tiles (U = 1), two per CU
             else:
-                k = 2 if W >= 5 else 1      # small tiles, two per CU, from W = 5 up
+                k = 0 if mode == 2 else 1
         else:
             k = max(n, 0)
         say(f"case W={W} rs={collective} mode={mode} cap={n} lds={lds} (per CU {L})")
