@@ -15,21 +15,27 @@ constexpr int kThreads = 256;   // one workgroup = four wave64s
 // kThreads * 4 * U elements and a thread holds W * U 16-byte loads in flight.
 // Chosen by measurement together with the workgroups per CU each launch
 // allows (the host's occupancy rule). For the
-// all-reduce (W read and W write streams), small tiles with two workgroups per
-// CU beat large tiles with one from W = 5 up (one workgroup's stores overlap
-// the other's loads), and W = 2 runs small tiles uncapped; W = 1, 3 and 4
-// keep four groups. The reduce-scatter (W reads, one write) keeps the larger
-// tiles up to W = 8.
-constexpr int unroll_for(int W, bool reduce_scatter)
+// all-reduce of fp32 gradients (W read and W write streams), small tiles with
+// two workgroups per CU beat large tiles with one from W = 5 up (one
+// workgroup's stores overlap the other's loads), and W = 2 runs small tiles
+// uncapped; W = 1, 3 and 4 keep four groups. Accumulating bf16 wgrads into
+// fp32 main_grad at W = 16 does better with two groups and one workgroup per
+// CU (at W = 8 both shapes measured the same; the generic kernel, W = 9..15,
+// loses with larger tiles, which only add serial passes; W = 32 would spill
+// registers). The reduce-scatter (W reads, one write) keeps the larger tiles
+// up to W = 8.
+// bf16_accum: input mode DDP_IN_BF16_ACCUM_F32.
+constexpr int unroll_for(int W, bool reduce_scatter, bool bf16_accum)
 {
     if (reduce_scatter) return W <= 4 ? 4 : (W <= 8 ? 2 : 1);
+    if (bf16_accum && W == 16) return 2;
     return (W == 2 || W >= 5) ? 1 : 4;
 }
 
 // Elements one workgroup covers (one tile).
-constexpr int64_t tile_elems(int W, bool reduce_scatter)
+constexpr int64_t tile_elems(int W, bool reduce_scatter, bool bf16_accum)
 {
-    return int64_t(kThreads) * 4 * unroll_for(W, reduce_scatter);
+    return int64_t(kThreads) * 4 * unroll_for(W, reduce_scatter, bf16_accum);
 }
 
 // A run of bucket elements that lies inside one gradient tensor and one ring

@@ -257,8 +257,8 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
                                             float *const (&ds)[NOUT], const bool (&on)[W], const DeviceSeg &sg,
                                             int64_t tin, const Scale &sc)
 {
-    constexpr int U = unroll_for(W, RS);
-    constexpr int64_t TILE = tile_elems(W, RS);
+    constexpr int U = unroll_for(W, RS, MODE == MODE_BF16);
+    constexpr int64_t TILE = tile_elems(W, RS, MODE == MODE_BF16);
     const int tid = int(threadIdx.x);
     int64_t e[U], el[U];
     bool ok[U];
@@ -313,7 +313,7 @@ template <int W, int MODE, int HOOK, bool RS, bool USED>
 __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, Scale sc)
 {
     constexpr int NOUT = RS ? 1 : W;
-    constexpr int64_t TILE = tile_elems(W, RS);
+    constexpr int64_t TILE = tile_elems(W, RS, MODE == MODE_BF16);
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);
@@ -372,7 +372,7 @@ template <int MODE, int HOOK>
 __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32_t tile_begin, Scale sc, int W,
                                                            int rs)
 {
-    const int64_t TILE = tile_elems(W, rs != 0);
+    const int64_t TILE = tile_elems(W, rs != 0, MODE == MODE_BF16);
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);

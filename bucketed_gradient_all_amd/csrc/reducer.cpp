@@ -54,17 +54,18 @@ std::string list_params(const std::vector<int32_t> &ps)
 // dispatcher keeps at most this many workgroups on a CU. Fewer tiles in
 // flight keep each of the 2W streams' in-flight window narrow (a few MiB
 // across the chip), which measured 2-8% faster than full occupancy for
-// W >= 3: one per CU with the large tiles (U = 4), two with the small ones
-// (U = 1, either input mode) and for the reduce-scatter. W <= 2 (four
-// streams), and the all-reduce of bf16 wgrads into fp32 main_grad with large
-// tiles (W = 3, 4: never measured capped), run at full occupancy.
+// W >= 3: one per CU with the larger tiles (U = 4 for fp32 gradients, U = 2
+// for bf16 wgrads at W = 16), two with the small ones (U = 1) and for the
+// reduce-scatter. W <= 2 (four streams), and the all-reduce of bf16 wgrads
+// into fp32 main_grad at W = 3, 4 (never measured capped), run at full
+// occupancy.
 // bf16_accum: input mode DDP_IN_BF16_ACCUM_F32.
 constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum)
 {
     if (W <= 2) return 0;
     if (reduce_scatter) return 2;
-    if (ddp::unroll_for(W, false) == 1) return 2;
-    return bf16_accum ? 0 : 1;
+    if (ddp::unroll_for(W, false, bf16_accum) == 1) return 2;
+    return bf16_accum && W <= 4 ? 0 : 1;
 }
 
 constexpr size_t kAlign = 256;
@@ -94,7 +95,7 @@ struct PlanView {
 // chunk of bucket element e is e / q with q = ceil(n / W) [DDP-ch17 §17.4].
 int build_segments(PlanView &pv, bool split_by_param)
 {
-    const int64_t TILE = ddp::tile_elems(pv.W, pv.reduce_scatter);
+    const int64_t TILE = ddp::tile_elems(pv.W, pv.reduce_scatter, pv.mode == DDP_IN_BF16_ACCUM_F32);
     pv.segs.clear();
     pv.tile_seg.clear();
     pv.tile_begin.assign(pv.B, 0);

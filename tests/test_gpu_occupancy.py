@@ -19,7 +19,8 @@ def _lds_per_cu():
 
 
 @pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (4, 0, 0), (4, 0, 2), (6, 0, 1), (8, 0, 0), (8, 1, 0),
-                                               (8, 0, 2), (16, 0, 0), (12, 0, 0), (16, 0, 2), (16, 1, 2)])
+                                               (8, 0, 2), (16, 0, 0), (12, 0, 0), (12, 0, 2), (16, 0, 2), (16, 1, 2),
+                                               (32, 0, 2)])
 def test_results_do_not_depend_on_the_cap(W, collective, mode):
     wl = _small_workload(5100 + W + collective, W, mode)
     run = Run(wl, collective=collective)
@@ -31,10 +32,12 @@ def test_results_do_not_depend_on_the_cap(W, collective, mode):
         if n == 0:
             if W <= 2:
                 k = 0
-            elif collective or W >= 5:
-                k = 2                       # reduce-scatter; small tiles (U = 1), two per CU
+            elif collective:
+                k = 2
+            elif mode == 2:                 # bf16 wgrads: U = 2 at one per CU at W = 16
+                k = 0 if W <= 4 else (1 if W == 16 else 2)
             else:
-                k = 0 if mode == 2 else 1
+                k = 2 if W >= 5 else 1      # small tiles (U = 1), two per CU, from W = 5 up
         else:
             k = max(n, 0)
         say(f"case W={W} rs={collective} mode={mode} cap={n} lds={lds} (per CU {L})")
