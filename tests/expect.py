@@ -110,14 +110,22 @@ def sample_positions(wl: Workload, plan, per_param: int, rng: np.random.Generato
 
 
 def expected_at(wl: Workload, plan, positions: List[Tuple[int, int]], seed: int,
-                hook: int = 0) -> Tuple[np.ndarray, np.ndarray]:
-    """Flat element indices of `positions` and the oracle's value there."""
+                hook: int = 0, used=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Flat element indices of `positions` and the oracle's value there.
+    used[w][p] == 0: replica w's slice of p is zero-filled; positions of
+    gradients no replica used are skipped (they are not written)."""
     sc = _scale(wl)
     W = wl.world
     by_param: Dict[int, List[int]] = {}
     for p, i in positions:
+        if used is not None and not any(used[w][p] for w in range(W)):
+            continue
         by_param.setdefault(p, []).append(i)
     flat_idx, vals = [], []
+
+    def on(w, p):
+        return used is None or bool(used[w][p])
+
     for p, idx in by_param.items():
         idx = np.asarray(idx, np.int64)
         b = plan.bucket_of[p]
@@ -125,17 +133,19 @@ def expected_at(wl: Workload, plan, positions: List[Tuple[int, int]], seed: int,
         e = plan.offset_in_bucket[p] // 4 + idx
         if wl.input_mode == IN_BF16_ACCUM_F32:
             mv = np.stack([synth.host_gather_f32(synth.key(seed, STREAM_MAIN, w, p), wl.dist, sc, idx)
-                           for w in range(W)], axis=1)
+                           if on(w, p) else np.zeros(idx.size, np.float32) for w in range(W)], axis=1)
             gv = np.stack([synth.host_gather_bf16(synth.key(seed, STREAM_WGRAD, w, p), wl.dist, sc, idx)
-                           for w in range(W)], axis=1)
+                           if on(w, p) else np.zeros(idx.size, np.uint16) for w in range(W)], axis=1)
             v = (compress.compressed_reduce_at(HOOK_FORMATS[hook], n, e, mv, gv) if hook
                  else fold.reduce_at_bf16acc(n, e, mv, gv))
         else:
             xv = np.stack([synth.host_gather_f32(synth.key(seed, STREAM_GRAD, w, p), wl.dist, sc, idx)
-                           for w in range(W)], axis=1)
+                           if on(w, p) else np.zeros(idx.size, np.float32) for w in range(W)], axis=1)
             v = compress.compressed_reduce_at(HOOK_FORMATS[hook], n, e, xv) if hook else fold.reduce_at_f32(n, e, xv)
         flat_idx.append(plan.bucket_offset[b] // 4 + e)
         vals.append(v)
+    if not flat_idx:
+        return np.zeros(0, np.int64), np.zeros(0, np.float32)
     return np.concatenate(flat_idx), np.concatenate(vals)
 
 

@@ -168,3 +168,72 @@ def test_sixty_four_replicas_is_the_mask_limit():
     ddp.ddp_finish(run.r, host_blocking=True)
     check(run, used, before)
     run.close()
+
+
+# ------------------------------------------------------ full size, sampled
+def _seeded_used(W, P, seed, pair_frac=0.2, global_frac=0.05):
+    rng = np.random.default_rng(seed)
+    used = (rng.random((W, P)) >= pair_frac).astype(np.uint8)
+    used[:, rng.random(P) < global_frac] = 0
+    return used
+
+
+def _sampled_with_unused(wl, used, hook=0, collective=0, replicas=(0, -1)):
+    """Runs one synchronized backward with the used table and compares
+    replicas' flat buffers at sampled elements: the oracle's value where the
+    replica's output is written, the previous contents elsewhere (gradients no
+    replica used; chunks another replica owns under reduce-scatter)."""
+    torch = _torch()
+    from expect import expected_at, oracle_plan, sample_positions
+    W, P = wl.world, len(wl.numel)
+    run = URun(wl, collective)
+    ddp = run.ddp
+    ddp.ddp_register_builtin_hook(run.r, hook)
+    oplan = oracle_plan(wl)
+    pos = sample_positions(wl, oplan, 16, np.random.default_rng(7))
+    flat_of = {p: (oplan.bucket_offset[oplan.bucket_of[p]] + oplan.offset_in_bucket[p]) // 4 for p in range(P)}
+    all_idx = np.unique(np.array([flat_of[p] + i for p, i in pos], np.int64))
+    sel = torch.from_numpy(all_idx).to("cuda")
+    reps = sorted({r % W for r in replicas})
+    before = {w: run.inputs.flat[w][sel].cpu().numpy() for w in reps}
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_set_local_used(run.r, used)
+    unused = {p for p in range(P) if not used[:, p].any()}
+    ddp.ddp_mark_ready_many(run.r, [p for p in range(P - 1, -1, -1) if p not in unused])
+    ddp.ddp_finish(run.r, host_blocking=True)
+    idx, want = expected_at(wl, oplan, pos, wl.seed, hook=hook, used=used)
+    order = np.argsort(idx)
+    idx_s, want_s = idx[order], want[order]
+    k = np.minimum(np.searchsorted(idx_s, all_idx), idx_s.size - 1)
+    written = idx_s[k] == all_idx
+    assert (~written).sum() > 0 and written.sum() > 0
+    for w in reps:
+        got = run.inputs.flat[w][sel].cpu().numpy()
+        m = written & (owned_mask(run, w)[all_idx] if collective else True)
+        assert_bits(got[m], want_s[k[m]], f"{wl.name} replica {w} reduced")
+        assert_bits(got[~m], before[w][~m], f"{wl.name} replica {w} untouched")
+    run.close()
+
+
+def test_megatron_sampled_with_unused_masks():
+    """Llama-1B shapes, W = 16, bf16 wgrads into fp32 main_grad: a seeded
+    used table (a fifth of the replica-gradient pairs unused, some gradients
+    unused everywhere)."""
+    from synth import workloads as wls
+    wl = wls.megatron_llama1b()
+    say("case megatron unused sampled")
+    _sampled_with_unused(wl, _seeded_used(wl.world, len(wl.numel), 11))
+
+
+def test_megatron_reduce_scatter_sampled_with_unused_masks():
+    from synth import workloads as wls
+    wl = wls.megatron_llama1b()
+    say("case megatron reduce-scatter unused sampled")
+    _sampled_with_unused(wl, _seeded_used(wl.world, len(wl.numel), 12), collective=1, replicas=(0, 5, 15))
+
+
+def test_bert_large_sampled_with_unused_masks_and_bf16_hook():
+    from synth import workloads as wls
+    wl = wls.bert_large()
+    say("case bert_large unused + bf16 hook sampled")
+    _sampled_with_unused(wl, _seeded_used(wl.world, len(wl.numel), 13), hook=1)
