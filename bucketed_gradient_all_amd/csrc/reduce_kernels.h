@@ -29,8 +29,10 @@
 //     tensor and one ring chunk, so a workgroup has one source tensor and one
 //     fold order (wave-uniform addresses in scalar registers, no per-lane
 //     branching on the chunk);
-//   * the fold order is fixed at compile time by loading replica (c + k) mod W
-//     into register slot k, so the order is a plain slot-0..W-1 sum;
+//   * the fold order is fixed by loading replica (c + k) mod W into register
+//     slot k, so the order is a plain slot-0..W-1 sum; W is a compile-time
+//     constant for W = 1..8, 16, 32, and W = 9..31 run the 16- or 32-slot
+//     instance with the slots past W switched off;
 //   * 16-byte vector loads and stores (8-byte for bf16), every load of a
 //     thread issued before the first add, non-temporal hints on the streamed
 //     data so it does not evict other lines from L2 / MALL.
@@ -224,26 +226,50 @@ __device__ __forceinline__ void scalar_parts(const KernelTables &T, const Device
     }
 }
 
-// One element with W known at compile time, from hoisted pointers; the sum
-// goes to the NOUT destinations (all W replicas, or the chunk's owner).
-template <int W, int NOUT, int MODE, int HOOK, bool USED>
+// Replica slots of a kernel instance: W of them at compile time. With
+// PARTIAL the replica count n (n <= W) is known only at run time, and slots
+// k >= n are absent: not read, not added (adding a zero would turn a -0 sum
+// into +0) and not written. Such instances serve the replica counts without
+// an instance of their own, with the fixed instances' single pass (every
+// load before the first add) instead of the generic kernel's groups of eight.
+template <int W, bool PARTIAL>
+struct Slots {
+    int n;
+    __device__ __forceinline__ bool has(int k) const { return !PARTIAL || k < n; }
+    __device__ __forceinline__ int count() const { return PARTIAL ? n : W; }
+};
+
+// The division rule of an instance: fixed by W, or read from the Scale when
+// the replica count is only known at run time.
+template <int W, bool PARTIAL>
+constexpr int div_of()
+{
+    return PARTIAL ? DIV_RUNTIME : div_for(W);
+}
+
+// One element from hoisted pointers; the sum goes to the NOUT destinations
+// (all replicas, or the chunk's owner).
+template <int W, int NOUT, int MODE, int HOOK, bool USED, bool PARTIAL>
 __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
                                                   float *const (&ds)[NOUT], const bool (&on)[W], int64_t e,
-                                                  const Scale &sc)
+                                                  const Scale &sc, Slots<W, PARTIAL> slots)
 {
     float t[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-        if (!USED || on[k])
-            t[k] = term1<MODE, HOOK, div_for(W)>(ld1(xs[k] + e), MODE == MODE_BF16 ? ld1h(gs[k] + e) : 0, sc);
+        if (slots.has(k) && (!USED || on[k]))
+            t[k] = term1<MODE, HOOK, div_of<W, PARTIAL>()>(ld1(xs[k] + e), MODE == MODE_BF16 ? ld1h(gs[k] + e) : 0,
+                                                          sc);
         else
             t[k] = 0.0f;
     }
     float acc = t[0];
 #pragma unroll
-    for (int k = 1; k < W; ++k) acc = add1<HOOK>(acc, t[k]);
+    for (int k = 1; k < W; ++k)
+        if (slots.has(k)) acc = add1<HOOK>(acc, t[k]);
 #pragma unroll
-    for (int w = 0; w < NOUT; ++w) st1(ds[w] + e, acc);
+    for (int w = 0; w < NOUT; ++w)
+        if (NOUT == 1 || slots.has(w)) st1(ds[w] + e, acc);
 }
 
 // The 16-byte-vector part of one tile: U groups of 4 elements per thread.
@@ -252,13 +278,14 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // then all stores. CHECK = true: the segment's last tile, with per-lane
 // bounds; out-of-range lanes load the segment's first vector (in bounds, value
 // unused) and skip their stores.
-template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED>
+template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED, bool PARTIAL>
 __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
                                             float *const (&ds)[NOUT], const bool (&on)[W], const DeviceSeg &sg,
-                                            int64_t tin, const Scale &sc)
+                                            int64_t tin, const Scale &sc, Slots<W, PARTIAL> slots)
 {
-    constexpr int U = unroll_for(W, RS, MODE == MODE_BF16);
-    constexpr int64_t TILE = tile_elems(W, RS, MODE == MODE_BF16);
+    constexpr int U = PARTIAL ? 1 : unroll_for(W, RS, MODE == MODE_BF16);
+    constexpr int64_t TILE = int64_t(kThreads) * 4 * U;
+    constexpr int DIV = div_of<W, PARTIAL>();
     const int tid = int(threadIdx.x);
     int64_t e[U], el[U];
     bool ok[U];
@@ -272,8 +299,9 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
     u16x4 g[U][W];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-        if (USED && !on[k]) {
-            // a replica that did not use this gradient: zero-filled slice, not read
+        if (!slots.has(k) || (USED && !on[k])) {
+            // an absent slot, or a replica that did not use this gradient
+            // (zero-filled slice): not read
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 v[u][k] = f32x4{0, 0, 0, 0};
@@ -290,41 +318,50 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
     f32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        acc[u] = (USED && !on[0]) ? f32x4{0, 0, 0, 0} : term4<MODE, HOOK, div_for(W)>(v[u][0], g[u][0], sc);
+        acc[u] = (USED && !on[0]) ? f32x4{0, 0, 0, 0} : term4<MODE, HOOK, DIV>(v[u][0], g[u][0], sc);
 #pragma unroll
         for (int k = 1; k < W; ++k)
-            acc[u] = add4<HOOK>(acc[u], (USED && !on[k]) ? f32x4{0, 0, 0, 0}
-                                                         : term4<MODE, HOOK, div_for(W)>(v[u][k], g[u][k], sc));
+            if (slots.has(k))
+                acc[u] = add4<HOOK>(acc[u], (USED && !on[k]) ? f32x4{0, 0, 0, 0}
+                                                             : term4<MODE, HOOK, DIV>(v[u][k], g[u][k], sc));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
         if (ok[u]) {
 #pragma unroll
-            for (int w = 0; w < NOUT; ++w) st4(ds[w] + e[u], acc[u]);
+            for (int w = 0; w < NOUT; ++w)
+                if (NOUT == 1 || slots.has(w)) st4(ds[w] + e[u], acc[u]);
         }
 }
 
-// W known at compile time: fully unrolled over replicas and vector groups.
-// All table reads (segment, source and destination pointers) happen before
-// the first store, so they stay in scalar registers; a table read after a
-// store would have to go through the vector memory path and wait for every
-// outstanding store.
-template <int W, int MODE, int HOOK, bool RS, bool USED>
-__global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, Scale sc)
+// W slots at compile time: fully unrolled over replicas and vector groups.
+// With PARTIAL, n replicas (n <= W, known at run time) fill the first n
+// slots and the tiles are 4 elements per thread (the host's tiling for every
+// replica count these instances serve). All table reads (segment, source and
+// destination pointers) happen before the first store, so they stay in
+// scalar registers; a table read after a store would have to go through the
+// vector memory path and wait for every outstanding store.
+template <int W, int MODE, int HOOK, bool RS, bool USED, bool PARTIAL>
+__global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t tile_begin, Scale sc, int n)
 {
     constexpr int NOUT = RS ? 1 : W;
-    constexpr int64_t TILE = tile_elems(W, RS, MODE == MODE_BF16);
+    constexpr int64_t TILE = PARTIAL ? int64_t(kThreads) * 4 : tile_elems(W, RS, MODE == MODE_BF16);
+    const Slots<W, PARTIAL> slots{n};
+    const int nrep = slots.count();
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);
 
-    // slot k holds replica (chunk + k) mod W, so the fold is slot 0, 1, ..., W-1
+    // slot k holds replica (chunk + k) mod nrep, so the fold is slot 0, 1, ...
     const float *xs[W];
     const unsigned short *gs[W];
     float *ds[NOUT];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-        const int r = slot_replica(sg.chunk, k, W);
+        xs[k] = nullptr;
+        gs[k] = nullptr;
+        if (!slots.has(k)) continue;
+        const int r = slot_replica(sg.chunk, k, nrep);
         xs[k] = src_f32<MODE>(T, sg, r);
         gs[k] = MODE == MODE_BF16 ? src_bf16(T, sg, r) : nullptr;
     }
@@ -332,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
         ds[0] = T.flat[sg.chunk] + sg.flat;   // chunk c belongs to replica c
     } else {
 #pragma unroll
-        for (int w = 0; w < NOUT; ++w) ds[w] = T.flat[w] + sg.flat;
+        for (int w = 0; w < NOUT; ++w) ds[w] = slots.has(w) ? T.flat[w] + sg.flat : nullptr;
     }
 
     bool on[W];
@@ -340,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
         const uint64_t m = T.used[sg.param];
         if (m == 0) return;   // no replica used this gradient: leave it untouched
 #pragma unroll
-        for (int k = 0; k < W; ++k) on[k] = (m >> slot_replica(sg.chunk, k, W)) & 1;
+        for (int k = 0; k < W; ++k) on[k] = slots.has(k) && ((m >> slot_replica(sg.chunk, k, nrep)) & 1);
     } else {
 #pragma unroll
         for (int k = 0; k < W; ++k) on[k] = true;
@@ -349,25 +386,27 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
     const int tid = int(threadIdx.x);
     if (sg.head >= 0) {
         if (sg.head + (tin + 1) * TILE <= sg.len)
-            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED>(xs, gs, ds, on, sg, tin, sc);
+            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots);
         else if (sg.len - sg.head >= 4)
-            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED>(xs, gs, ds, on, sg, tin, sc);
+            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots);
         if (tin == 0) {
             const int64_t body = (sg.len - sg.head) / 4 * 4;
             const int64_t tail = sg.len - sg.head - body;
-            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED>(xs, gs, ds, on, tid, sc);
+            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, tid, sc, slots);
             if (tid >= 64 && tid < 64 + tail)
-                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED>(xs, gs, ds, on, sg.head + body + (tid - 64), sc);
+                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, sg.head + body + (tid - 64),
+                                                                      sc, slots);
         }
         return;
     }
     for (int64_t j = tid; j < TILE; j += kThreads) {
         const int64_t e = tin * TILE + j;
-        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED>(xs, gs, ds, on, e, sc);
+        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, e, sc, slots);
     }
 }
 
-// Any W: replicas are taken eight at a time, in fold order.
+// Any W the fixed and partial instances do not serve (above 32): replicas are
+// taken eight at a time, in fold order. It walks its tile with any tiling.
 template <int MODE, int HOOK>
 __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32_t tile_begin, Scale sc, int W,
                                                            int rs)
@@ -418,21 +457,25 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
     scalar_parts<MODE, HOOK>(T, sg, tin, TILE, sc, W, rs != 0);
 }
 
-template <int W, int MODE, int HOOK>
+// n: the replica count (at most W; below W only with PARTIAL).
+template <int W, int MODE, int HOOK, bool PARTIAL>
 hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc, bool rs,
-                        unsigned lds, hipStream_t st)
+                        unsigned lds, hipStream_t st, int n)
 {
     const dim3 g(n_tiles), b(kThreads);
     if (t.used) {
         if (rs)
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true>), g, b, lds, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true, PARTIAL>), g, b, lds, st, t, tile_begin, sc, n);
         else
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, true>), g, b, lds, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, true, PARTIAL>), g, b, lds, st, t, tile_begin, sc,
+                               n);
     } else {
         if (rs)
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, false>), g, b, lds, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, false, PARTIAL>), g, b, lds, st, t, tile_begin, sc,
+                               n);
         else
-            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, false>), g, b, lds, st, t, tile_begin, sc);
+            hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, false, false, PARTIAL>), g, b, lds, st, t, tile_begin,
+                               sc, n);
     }
     return hipGetLastError();
 }
@@ -442,17 +485,24 @@ hipError_t dispatch_w(int W, bool rs, const KernelTables &t, int32_t tile_begin,
                       unsigned lds, hipStream_t st)
 {
     switch (W) {
-    case 1: return launch_fixed<1, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 2: return launch_fixed<2, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 3: return launch_fixed<3, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 4: return launch_fixed<4, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 5: return launch_fixed<5, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 6: return launch_fixed<6, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 7: return launch_fixed<7, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 8: return launch_fixed<8, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 16: return launch_fixed<16, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
-    case 32: return launch_fixed<32, MODE, HOOK>(t, tile_begin, n_tiles, sc, rs, lds, st);
+    case 1: return launch_fixed<1, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 2: return launch_fixed<2, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 3: return launch_fixed<3, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 4: return launch_fixed<4, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 5: return launch_fixed<5, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 6: return launch_fixed<6, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 7: return launch_fixed<7, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 8: return launch_fixed<8, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 16: return launch_fixed<16, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 32: return launch_fixed<32, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
     default:
+        // the partial instances tile 4 elements per thread, as the host does
+        // for every replica count between 9 and 31 (checked, so that a change
+        // of the tiling rule falls back to the generic kernel)
+        if (W > 8 && W < 16 && unroll_for(W, rs, MODE == MODE_BF16) == 1)
+            return launch_fixed<16, MODE, HOOK, true>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+        if (W > 16 && W < 32 && unroll_for(W, rs, MODE == MODE_BF16) == 1)
+            return launch_fixed<32, MODE, HOOK, true>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
         hipLaunchKernelGGL((reduce_generic<MODE, HOOK>), dim3(n_tiles), dim3(kThreads), lds, st, t, tile_begin, sc,
                            W, rs ? 1 : 0);
         return hipGetLastError();

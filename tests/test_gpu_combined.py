@@ -33,7 +33,7 @@ def check_combined(run, used, hook, collective, before):
 @pytest.mark.parametrize("seed", range(24))
 def test_random_feature_combinations(seed):
     rng = random.Random(seed)
-    W = rng.choice([1, 2, 3, 4, 5, 8, 12, 16])
+    W = rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 24])
     mode = rng.choice([0, 1, 2])
     collective = rng.choice([0, 1])
     hook = rng.choice([0, 0, 1, 2])

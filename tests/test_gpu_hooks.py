@@ -35,7 +35,7 @@ def check_hook_full(run, hook, collective=0, before=None):
 
 
 @pytest.mark.parametrize("hook", [BF16_HOOK, FP16_HOOK])
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 32])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 24, 32])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_small_random_workloads_bit_exact(hook, W, mode):
     for seed in range(2):
@@ -48,7 +48,7 @@ def test_small_random_workloads_bit_exact(hook, W, mode):
 
 
 @pytest.mark.parametrize("hook", [BF16_HOOK, FP16_HOOK])
-@pytest.mark.parametrize("W", [2, 5, 8, 13])
+@pytest.mark.parametrize("W", [2, 5, 8, 13, 20])
 @pytest.mark.parametrize("mode", [0, 2])
 def test_reduce_scatter_with_hook(hook, W, mode):
     wl = _small_workload(8100 + 10 * W + mode, W, mode)
@@ -108,7 +108,7 @@ def _nan_aware_equal(got, want):
 
 
 @pytest.mark.parametrize("hook", [BF16_HOOK, FP16_HOOK])
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 14])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 14, 27])
 def test_rounding_edges_through_the_kernel(hook, W):
     """Values chosen at the formats' rounding boundaries (ties, overflow,
     subnormals, inf, and a NaN), on every replica at shifted positions, so

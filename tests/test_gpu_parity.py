@@ -124,7 +124,7 @@ def _small_workload(seed, W, mode):
                     first_cap_bytes=first, dist=dist, sigma=rng.choice([1e-3, 1.0]), input_mode=mode, seed=seed)
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 32])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 15, 16, 17, 24, 31, 32, 33])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_small_random_workloads_bit_exact(W, mode):
     for seed in range(3):
@@ -201,6 +201,39 @@ def test_nan_and_inf_propagate():
         out = run.flat_host(w)
         assert np.isnan(out[5]) and out[9] == np.inf and np.isnan(out[11])
         assert np.all(np.isfinite(np.delete(out, [5, 9, 11])))
+    run.close()
+
+
+@pytest.mark.parametrize("W", [3, 12, 16, 24, 40])
+@pytest.mark.parametrize("collective", [0, 1])
+@pytest.mark.parametrize("hook", [0, 1, 2])
+def test_negative_zero_survives_the_fold(W, collective, hook):
+    """An element that is -0 on every replica reduces to -0 (each term is -0,
+    and -0 + -0 = -0 in round-to-nearest); a +0 on any replica gives +0. A
+    kernel that added a zero for a replica slot it does not have (the 16- and
+    32-slot instances serve W = 9..31) would turn the first into +0."""
+    torch = _torch()
+    from synth.workloads import Workload, DIST_UNIFORM
+    n = 3000
+    wl = Workload(f"negzero_w{W}", [(n,)], world=W, cap_bytes=INF, first_cap_bytes=INF, dist=DIST_UNIFORM)
+    run = Run(wl, collective=collective)
+    run.ddp.ddp_register_builtin_hook(run.r, hook)
+    rng = np.random.default_rng(W)
+    pos_zero = rng.random(n) < 0.5          # elements where one replica holds +0
+    who = rng.integers(0, W, n)
+    for w in range(W):
+        x = np.full(n, -0.0, np.float32)
+        x[pos_zero & (who == w)] = 0.0
+        off = run.inputs.grad_off[0]
+        run.inputs.grads[w][off:off + 4 * n].view(torch.float32).copy_(torch.from_numpy(x))
+    before = [run.flat_host(w) for w in range(W)]
+    run.step()
+    want = np.where(pos_zero, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    for w in range(W):
+        got = run.flat_host(w)
+        m = owned_mask(run, w) if collective else np.ones(n, bool)
+        assert_bits(got[m], want[m], f"W={W} replica {w}")
+        assert_bits(got[~m], before[w][~m], f"W={W} replica {w} untouched")
     run.close()
 
 
@@ -400,7 +433,7 @@ def check_reduce_scatter(run, before):
         assert_bits(got[~m], before[w][~m], f"{wl.name} replica {w} untouched part")
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 7, 8, 12, 16, 32])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 7, 8, 9, 12, 16, 24, 32])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_reduce_scatter_small_workloads_bit_exact(W, mode):
     for seed in range(2):

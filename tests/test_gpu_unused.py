@@ -59,7 +59,7 @@ def check(run, used, before, collective=0):
         assert_bits(got[~m], before[w][~m], f"{wl.name} replica {w} untouched part")
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 8, 12, 16])
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 12, 16, 24])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("collective", [0, 1])
 def test_unused_slices_are_zero_and_globally_unused_untouched(W, mode, collective):
