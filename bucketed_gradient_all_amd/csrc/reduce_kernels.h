@@ -181,6 +181,14 @@ __device__ __forceinline__ uint64_t used_mask(const KernelTables &T, const Devic
     return T.used ? T.used[sg.param] : ~uint64_t(0);
 }
 
+// Whether replica r contributes under mask m. Masks exist for W <= 64 only;
+// replicas past 64 (W > 64, no masks) always contribute, and the shift stays
+// below 64.
+__device__ __forceinline__ bool replica_on(uint64_t m, int r)
+{
+    return r >= 64 || ((m >> r) & 1);
+}
+
 // One element, any W: used for unaligned heads and tails and for segments
 // whose pointers do not allow 16-byte vectors.
 template <int MODE, int HOOK>
@@ -191,7 +199,7 @@ __device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t 
     for (int k = 0; k < W; ++k) {
         const int r = slot_replica(sg.chunk, k, W);
         float t = 0.0f;
-        if ((m >> r) & 1) {
+        if (replica_on(m, r)) {
             float x = ld1(src_f32<MODE>(T, sg, r) + e);
             unsigned short g = MODE == MODE_BF16 ? ld1h(src_bf16(T, sg, r) + e) : 0;
             t = term1<MODE, HOOK, DIV_RUNTIME>(x, g, sc);
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
                     on[j] = false;
                     if (k0 + j < W) {
                         const int r = slot_replica(sg.chunk, k0 + j, W);
-                        on[j] = (m >> r) & 1;
+                        on[j] = replica_on(m, r);
                         if (on[j]) {
                             v[j] = ld4(src_f32<MODE>(T, sg, r) + e);
                             g[j] = MODE == MODE_BF16 ? ld4h(src_bf16(T, sg, r) + e) : u16x4{0, 0, 0, 0};

@@ -58,11 +58,13 @@ std::string list_params(const std::vector<int32_t> &ps)
 // for bf16 wgrads at W = 16), two with the small ones (U = 1) and for the
 // reduce-scatter. W <= 2 (four streams), and the all-reduce of bf16 wgrads
 // into fp32 main_grad at W = 3, 4 (never measured capped), run at full
-// occupancy.
+// occupancy. So does W > 32: the generic kernel loads eight replicas per
+// round trip and needs every resident workgroup to hide the latency
+// (capped at two per CU it ran a third slower).
 // bf16_accum: input mode DDP_IN_BF16_ACCUM_F32.
 constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum)
 {
-    if (W <= 2) return 0;
+    if (W <= 2 || W > 32) return 0;
     if (reduce_scatter) return 2;
     if (ddp::unroll_for(W, false, bf16_accum) == 1) return 2;
     return bf16_accum && W <= 4 ? 0 : 1;

@@ -20,7 +20,7 @@ def _lds_per_cu():
 
 @pytest.mark.parametrize("W,collective,mode", [(2, 0, 0), (4, 0, 0), (4, 0, 2), (6, 0, 1), (8, 0, 0), (8, 1, 0),
                                                (8, 0, 2), (16, 0, 0), (12, 0, 0), (12, 0, 2), (16, 0, 2), (16, 1, 2),
-                                               (32, 0, 2)])
+                                               (32, 0, 2), (40, 0, 0), (40, 1, 2)])
 def test_results_do_not_depend_on_the_cap(W, collective, mode):
     wl = _small_workload(5100 + W + collective, W, mode)
     run = Run(wl, collective=collective)
@@ -30,7 +30,7 @@ def test_results_do_not_depend_on_the_cap(W, collective, mode):
         ddp.ddp_set_workgroups_per_cu(run.r, n)
         lds = ddp.ddp_get_launch_lds(run.r)
         if n == 0:
-            if W <= 2:
+            if W <= 2 or W > 32:
                 k = 0
             elif collective:
                 k = 2
