@@ -82,7 +82,8 @@ def unused_table(wl, frac: float, global_frac: float, seed: int = 2024):
 
 
 class Session:
-    def __init__(self, wl, arena: bool = False, stagger=None, backward_kind: str = "spin", used=None):
+    def __init__(self, wl, arena: bool = False, stagger=None, backward_kind: str = "spin", used=None,
+                 streams=None):
         import numpy as np
         import torch
 
@@ -102,8 +103,7 @@ class Session:
         self.stagger = REPLICA_STAGGER if stagger is None else stagger
         self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena, stagger=self.stagger)
         log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
-        self.compute = torch.cuda.Stream()
-        self.comm = torch.cuda.Stream()
+        self.compute, self.comm = streams if streams is not None else (torch.cuda.Stream(), torch.cuda.Stream())
         self.used = used
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
                                   self.inputs.flat_ptrs(), self.compute.cuda_stream, self.comm.cuda_stream,
@@ -344,13 +344,19 @@ def run_sweep(args):
     coalesced), and the step with a synthetic backward overlapped and in
     series."""
     from synth import workloads as wls
+    import torch
     rows = []
     worlds = [int(x) for x in args.sweep_worlds.split(",")]
     caps = [int(x) for x in args.sweep_caps.split(",")]
+    # one stream pair for every configuration: a process that keeps creating
+    # stream pairs gets some whose two streams the runtime places so that they
+    # run one after the other (measured: the second pair of a process lost all
+    # overlap), which would make the overlap columns depend on the order
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
     for W in worlds:
         for cap in caps:
             wl = wls.sweep(W, cap)
-            s = Session(wl, backward_kind=args.backward_kind)
+            s = Session(wl, backward_kind=args.backward_kind, streams=streams)
             import bucketed_gradient_all_amd as ddp
             ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
             nbytes = wl.algorithmic_bytes()
