@@ -301,14 +301,17 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
 /* Workgroups of one reduction launch that may share a CU. The kernel uses no
  * LDS; a launch reserves LDS only so that the hardware dispatcher keeps at
  * most n of its workgroups on a CU. Fewer tiles in flight keep the 2W
- * streams' windows narrow, which suits HBM: on MI355X this measured 4-8%
- * faster than full occupancy for fp32 inputs and W >= 3. The reserved LDS is
- * unavailable to kernels that share the CUs; with a GEMM backward running
- * beside the reduction the cap still measured no worse, but a caller whose
- * backward kernels need that LDS may prefer no cap.
- *   n = 0  automatic (default): none for W <= 2 and for the all-reduce in
- *          DDP_IN_BF16_ACCUM_F32 mode; two per CU for reduce-scatter and
- *          for W >= 9; one per CU otherwise;
+ * streams' windows narrow, which suits HBM: on MI355X this measured 2-8%
+ * faster than full occupancy for 3 <= W <= 32. The reserved LDS is
+ * unavailable to kernels that share the CUs: with bf16 GEMMs running beside
+ * the reduction as the backward, BERT-large's overlapped step was about
+ * 0.6 ms (3%) shorter at n = 1 than at the automatic two per CU, so a caller
+ * whose backward kernels need LDS may prefer n = 1, or no cap.
+ *   n = 0  automatic (default): none for W <= 2 and for W > 32; two per CU
+ *          for the reduce-scatter and for the all-reduce at W = 5..32;
+ *          except that the all-reduce at W = 3, 4 runs one per CU (none in
+ *          DDP_IN_BF16_ACCUM_F32 mode) and the DDP_IN_BF16_ACCUM_F32
+ *          all-reduce at W = 16 runs one per CU;
  *   n < 0  no cap (no LDS reserved; occupancy limited by registers only);
  *   1..8   at most n per CU.
  * Takes effect at the next launch; results do not depend on it.
