@@ -122,7 +122,7 @@ enum {
 typedef struct ddp_reducer ddp_reducer;   /* opaque, owned by the library */
 
 typedef struct {
-    int32_t world;                     /* W >= 1 replicas                                           */
+    int32_t world;                     /* W replicas, 1 <= W <= 1024 (<= 64 with find_unused)      */
     int32_t n_params;                  /* P >= 0                                                    */
     const int64_t *param_numel;        /* [P] elements per gradient                                 */
     const int32_t *bucket_of;          /* [P] a plan (e.g. from ddp_plan_buckets)                   */
