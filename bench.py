@@ -43,6 +43,17 @@ def host_cores() -> int:
         return os.cpu_count() or 1
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 HOOKS = {"none": 0, "bf16": 1, "fp16": 2}          # DDP_HOOK_ALLREDUCE, _BF16_COMPRESS, _FP16_COMPRESS
 HOOK_FORMATS = {1: "bf16", 2: "fp16"}
 
@@ -334,6 +345,8 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0, used=None):
                   f"generation untimed",
         "single_thread_value": round(gbps_1, 3),
         "cpu_seconds": round(t1 + tmt, 2),
+        "cpu_model": host_cpu_model(),
+        "host_cpus": os.cpu_count(),
         "gpu_matches_oracle_on_sample": match,
     }
 
