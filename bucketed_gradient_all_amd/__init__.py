@@ -53,20 +53,38 @@ SOURCES = ["reducer.cpp", "bucket_reduce.hip", "bucket_bf16_hook.hip", "bucket_f
 HEADERS = ["internal.h", "reduce_kernels.h"]
 
 
+BUILD_DIR = os.path.join(HERE, "_build")
+
+
+def resource_report_path(src: str) -> str:
+    """Where build() keeps the compiler's per-kernel resource report of a
+    kernel source (registers, scratch, occupancy)."""
+    return os.path.join(BUILD_DIR, src.replace(".", "_") + ".resources.txt")
+
+
 def build(verbose: bool = False) -> None:
-    """Compile libddp.so in place with hipcc for gfx950."""
-    objdir = os.path.join(HERE, "_build")
-    os.makedirs(objdir, exist_ok=True)
+    """Compile libddp.so in place with hipcc for gfx950. For the kernel
+    sources the compiler's resource report is kept beside the objects."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
     procs, objs = [], []
     for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".", "_") + ".o")
+        obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
         cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj,
                os.path.join(CSRC, src)]
+        report = None
+        if src.endswith(".hip"):
+            cmd.append("-Rpass-analysis=kernel-resource-usage")
+            report = open(resource_report_path(src), "w")
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((cmd, subprocess.Popen(cmd, cwd=HERE)))
+        procs.append((cmd, subprocess.Popen(cmd, cwd=HERE, stderr=report), report))
         objs.append(obj)
-    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    failed = []
+    for cmd, p, report in procs:
+        if p.wait() != 0:
+            failed.append(cmd)
+        if report is not None:
+            report.close()
     if failed:
         raise subprocess.CalledProcessError(1, failed[0])
     cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB_PATH + ".tmp", *objs]
