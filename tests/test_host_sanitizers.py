@@ -1,0 +1,48 @@
+"""The host half of the library (planner, reducer state machine, groups,
+masks, failure handling) built with g++ under AddressSanitizer and
+UndefinedBehaviorSanitizer, and driven by tests/native/host_fuzz.cpp: random
+API sequences on host-only reducers, whose launches go to a callback. The
+kernel launchers are stubbed out (a host-only reducer never launches one);
+no GPU is needed."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bucketed_gradient_all_amd", "csrc")
+
+STUB = r'''
+#include "internal.h"
+namespace ddp {
+hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned, hipStream_t)
+{ return hipErrorInvalidValue; }
+hipError_t launch_bf16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned,
+                            hipStream_t)
+{ return hipErrorInvalidValue; }
+hipError_t launch_fp16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned,
+                            hipStream_t)
+{ return hipErrorInvalidValue; }
+}
+'''
+
+
+def test_host_logic_under_sanitizers(tmp_path):
+    if shutil.which("g++") is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("needs g++ and the ROCm headers")
+    stub = tmp_path / "stub.cpp"
+    stub.write_text(STUB)
+    exe = tmp_path / "host_fuzz"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-static-libasan", "-static-libubsan",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "reducer.cpp"), str(stub), os.path.join(ROOT, "tests", "native", "host_fuzz.cpp"),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", str(exe)]
+    subprocess.run(cmd, check=True, timeout=600)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([str(exe), "300"], capture_output=True, text=True, timeout=600, env=env)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "host_fuzz ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
