@@ -30,7 +30,11 @@
  * buffer of 16 * P bytes (hipHostMalloc), freed by ddp_reducer_destroy.
  *
  * Threading: a reducer is used from one thread at a time (hooks fire from
- * one thread, [DDP-ch17 §17.12]). ddp_last_error() text is per thread.
+ * one thread, [DDP-ch17 §17.12]); that thread may change between calls, as
+ * when autograd runs gradient hooks on its device worker thread while the
+ * caller's thread waits in backward and calls ddp_finish afterwards.
+ * Calls on different reducers may run concurrently. ddp_last_error() text is
+ * per thread: read it on the thread whose call failed.
  */
 #ifndef DDP_H
 #define DDP_H
