@@ -50,14 +50,18 @@ struct DeviceSeg {
     int32_t tile0;   // first tile of this segment
     int32_t head;    // scalar elements (0..63) before the aligned vector body,
                      // or -1: the segment is processed one element per lane
+    uint64_t used;   // bit w: replica w contributes the segment's gradient (unused
+                     // detection; all ones otherwise). Part of the record so that a
+                     // tile fetches its segment and its mask in one round trip.
 };
+static_assert(sizeof(DeviceSeg) == 48, "segment records are three 16-byte loads");
 
 struct KernelTables {
     const DeviceSeg *segs;
     const int32_t *tile_seg;       // tile -> segment
     const void *const *grads;      // [W*P] replica-major source pointers (COPY, BF16_ACCUM)
     float *const *flat;            // [W] flat buffers
-    const uint64_t *used;          // [P] bit w: replica w contributes gradient p (unused detection), or null
+    int32_t masked;                // unused detection: the segments' replica masks apply
     int32_t n_params;
 };
 
@@ -73,9 +77,9 @@ struct Scale {
 // Each enqueues tiles [tile_begin, tile_begin + n_tiles) of the table on
 // stream s: all-reduce (the sum stored to every replica) or reduce-scatter
 // (chunk c stored to replica c only), and returns hipSuccess or the launch
-// error. With t.used set, a replica whose bit is clear contributes a
-// zero-filled slice (its source is not read) and a gradient no replica used
-// is not written at all.
+// error. With t.masked set (unused detection), a replica whose bit in the
+// segment's mask is clear contributes a zero-filled slice (its source is not
+// read) and a gradient no replica used is not written at all.
 //   launch_mean:       the fp32 mean (no communication hook)
 //   launch_bf16_hook:  through the bf16 compression hook
 //   launch_fp16_hook:  through the fp16 compression hook

@@ -95,6 +95,30 @@ __device__ __forceinline__ u16x4 ld4h(const unsigned short *p)
     return __builtin_nontemporal_load((const GLOBAL u16x4 *)(p));
 }
 
+// Masked loads through a buffer resource (a base address and a byte range):
+// a load at an offset outside the range returns zero without touching
+// memory, so a replica that did not use a gradient gets range 0 and its
+// loads cost no memory traffic, with no branch and no address select. The
+// third dword is the gfx9 default (32-bit data format, untyped access); the
+// aux operand 2 is the nontemporal hint the global loads use.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNT = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_of(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ f32x4 ld4_in(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, kLoadNT));
+}
+
+__device__ __forceinline__ u16x4 ld4h_in(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(u16x4, __builtin_amdgcn_raw_buffer_load_b64(r, int(byte_off), 0, kLoadNT));
+}
+
 __device__ __forceinline__ void st4(float *p, f32x4 v)
 {
     __builtin_nontemporal_store(v, (GLOBAL f32x4 *)(p));
@@ -176,11 +200,6 @@ __device__ __forceinline__ const unsigned short *src_bf16(const KernelTables &T,
     return static_cast<const unsigned short *>(T.grads[int64_t(r) * T.n_params + sg.param]) + sg.src;
 }
 
-__device__ __forceinline__ uint64_t used_mask(const KernelTables &T, const DeviceSeg &sg)
-{
-    return T.used ? T.used[sg.param] : ~uint64_t(0);
-}
-
 // Whether replica r contributes under mask m. Masks exist for W <= 64 only;
 // replicas past 64 (W > 64, no masks) always contribute, and the shift stays
 // below 64.
@@ -192,9 +211,9 @@ __device__ __forceinline__ bool replica_on(uint64_t m, int r)
 // One element, any W: used for unaligned heads and tails and for segments
 // whose pointers do not allow 16-byte vectors.
 template <int MODE, int HOOK>
-__device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t e, const Scale &sc, int W, bool rs)
+__device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, uint64_t m, int64_t e, const Scale &sc, int W,
+                            bool rs)
 {
-    const uint64_t m = used_mask(T, sg);
     float acc = 0.0f;
     for (int k = 0; k < W; ++k) {
         const int r = slot_replica(sg.chunk, k, W);
@@ -215,22 +234,22 @@ __device__ void fold_scalar(const KernelTables &T, const DeviceSeg &sg, int64_t 
 
 // Heads, tails and scalar-only segments of a tile.
 template <int MODE, int HOOK>
-__device__ __forceinline__ void scalar_parts(const KernelTables &T, const DeviceSeg &sg, int64_t tin, int64_t tile,
-                                             const Scale &sc, int W, bool rs)
+__device__ __forceinline__ void scalar_parts(const KernelTables &T, const DeviceSeg &sg, uint64_t m, int64_t tin,
+                                             int64_t tile, const Scale &sc, int W, bool rs)
 {
     const int tid = threadIdx.x;
     if (sg.head >= 0) {
         if (tin != 0) return;
         const int64_t body = (sg.len - sg.head) / 4 * 4;
         const int64_t tail = sg.len - sg.head - body;
-        if (tid < sg.head) fold_scalar<MODE, HOOK>(T, sg, tid, sc, W, rs);
-        if (tid >= 64 && tid < 64 + tail) fold_scalar<MODE, HOOK>(T, sg, sg.head + body + (tid - 64), sc, W, rs);
+        if (tid < sg.head) fold_scalar<MODE, HOOK>(T, sg, m, tid, sc, W, rs);
+        if (tid >= 64 && tid < 64 + tail) fold_scalar<MODE, HOOK>(T, sg, m, sg.head + body + (tid - 64), sc, W, rs);
         return;
     }
     const int64_t base = tin * tile;
     for (int64_t j = tid; j < tile; j += kThreads) {
         const int64_t e = base + j;
-        if (e < sg.len) fold_scalar<MODE, HOOK>(T, sg, e, sc, W, rs);
+        if (e < sg.len) fold_scalar<MODE, HOOK>(T, sg, m, e, sc, W, rs);
     }
 }
 
@@ -260,7 +279,7 @@ constexpr int div_of()
 template <int W, int NOUT, int MODE, int HOOK, bool USED, bool PARTIAL>
 __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
                                                   float *const (&ds)[NOUT], const bool (&on)[W], int64_t e,
-                                                  const Scale &sc, Slots<W, PARTIAL> slots)
+                                                  const Scale &sc, Slots<W, PARTIAL> slots, bool write)
 {
     float t[W];
 #pragma unroll
@@ -275,6 +294,7 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 #pragma unroll
     for (int k = 1; k < W; ++k)
         if (slots.has(k)) acc = add1<HOOK>(acc, t[k]);
+    if (!write) return;
 #pragma unroll
     for (int w = 0; w < NOUT; ++w)
         if (NOUT == 1 || slots.has(w)) st1(ds[w] + e, acc);
@@ -284,36 +304,63 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // CHECK = false: the whole tile lies inside the segment body (the common
 // case), so the block is straight-line code: all W*U loads, then the folds,
 // then all stores. CHECK = true: the segment's last tile, with per-lane
-// bounds; out-of-range lanes load the segment's first vector (in bounds, value
-// unused) and skip their stores.
+// bounds; out-of-range lanes load an in-bounds vector (value unused) and skip
+// their stores.
+//
+// With USED the loads go through buffer resources over this tile of each
+// replica's source: a replica that did not use the gradient gets range 0,
+// so its loads return the zero-filled slice its term is defined by (a +0
+// input) and read nothing, with no branch; an out-of-range lane of the last
+// tile gets an offset past every range and reads nothing either.
 template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED, bool PARTIAL>
 __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
                                             float *const (&ds)[NOUT], const bool (&on)[W], const DeviceSeg &sg,
-                                            int64_t tin, const Scale &sc, Slots<W, PARTIAL> slots)
+                                            int64_t tin, const Scale &sc, Slots<W, PARTIAL> slots, bool write)
 {
     constexpr int U = PARTIAL ? 1 : unroll_for(W, RS, MODE == MODE_BF16);
     constexpr int64_t TILE = int64_t(kThreads) * 4 * U;
     constexpr int DIV = div_of<W, PARTIAL>();
+    constexpr uint32_t kPast = 0x3FFFFFF0u;   // an element offset past every range (x4 bytes still fits)
     const int tid = int(threadIdx.x);
+    const int64_t t0 = sg.head + tin * TILE;   // the tile's first element
     int64_t e[U], el[U];
+    uint32_t rel[U];   // element offset from t0 (USED loads)
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        e[u] = sg.head + tin * TILE + int64_t(u * kThreads + tid) * 4;
+        const int64_t r = int64_t(u * kThreads + tid) * 4;
+        e[u] = t0 + r;
         ok[u] = !CHECK || e[u] + 4 <= sg.len;
-        el[u] = ok[u] ? e[u] : int64_t(sg.head);
+        el[u] = ok[u] ? e[u] : int64_t(sg.head);   // the segment's first vector: in bounds
+        rel[u] = ok[u] ? uint32_t(r) : kPast;
     }
+    // elements of this tile inside the segment (the last tile may hold fewer,
+    // or none past its head: t0 can exceed len by less than one vector group)
+    const uint32_t span = CHECK ? uint32_t(sg.len > t0 ? (sg.len - t0 < TILE ? sg.len - t0 : TILE) : 0)
+                                : uint32_t(TILE);
     f32x4 v[U][W];
     u16x4 g[U][W];
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-        if (!slots.has(k) || (USED && !on[k])) {
-            // an absent slot, or a replica that did not use this gradient
-            // (zero-filled slice): not read
+        if (!slots.has(k)) {   // an absent slot: nothing to read
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 v[u][k] = f32x4{0, 0, 0, 0};
                 g[u][k] = u16x4{0, 0, 0, 0};
+            }
+            continue;
+        }
+        if (USED) {
+            const __amdgpu_buffer_rsrc_t rx = range_of(xs[k] + t0, on[k] ? 4 * span : 0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u][k] = ld4_in(rx, 4 * rel[u]);
+            if (MODE == MODE_BF16) {
+                const __amdgpu_buffer_rsrc_t rg = range_of(gs[k] + t0, on[k] ? 2 * span : 0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) g[u][k] = ld4h_in(rg, 2 * rel[u]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) g[u][k] = u16x4{0, 0, 0, 0};
             }
             continue;
         }
@@ -326,16 +373,14 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
     f32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        acc[u] = (USED && !on[0]) ? f32x4{0, 0, 0, 0} : term4<MODE, HOOK, DIV>(v[u][0], g[u][0], sc);
+        acc[u] = term4<MODE, HOOK, DIV>(v[u][0], g[u][0], sc);
 #pragma unroll
         for (int k = 1; k < W; ++k)
-            if (slots.has(k))
-                acc[u] = add4<HOOK>(acc[u], (USED && !on[k]) ? f32x4{0, 0, 0, 0}
-                                                             : term4<MODE, HOOK, DIV>(v[u][k], g[u][k], sc));
+            if (slots.has(k)) acc[u] = add4<HOOK>(acc[u], term4<MODE, HOOK, DIV>(v[u][k], g[u][k], sc));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (ok[u]) {
+        if (ok[u] && write) {
 #pragma unroll
             for (int w = 0; w < NOUT; ++w)
                 if (NOUT == 1 || slots.has(w)) st4(ds[w] + e[u], acc[u]);
@@ -358,6 +403,7 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
     const int nrep = slots.count();
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
+    const uint64_t m = USED ? sg.used : ~uint64_t(0);
     const int64_t tin = int64_t(tile - sg.tile0);
 
     // slot k holds replica (chunk + k) mod nrep, so the fold is slot 0, 1, ...
@@ -373,17 +419,29 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
         xs[k] = src_f32<MODE>(T, sg, r);
         gs[k] = MODE == MODE_BF16 ? src_bf16(T, sg, r) : nullptr;
     }
-    if (RS) {
+    if (MODE != MODE_COPY) {
+        // The sources are the flat buffers themselves (VIEW input, bf16-mode
+        // main_grad). Slot k reads replica (chunk + k) mod n, so slot 0 is the
+        // chunk's owner and the slots cover every replica once: the stores go
+        // through the source pointers, and no second set of W pointers takes
+        // scalar registers.
+#pragma unroll
+        for (int w = 0; w < NOUT; ++w) ds[w] = slots.has(w) ? const_cast<float *>(xs[w]) : nullptr;
+    } else if (RS) {
         ds[0] = T.flat[sg.chunk] + sg.flat;   // chunk c belongs to replica c
     } else {
 #pragma unroll
         for (int w = 0; w < NOUT; ++w) ds[w] = slots.has(w) ? T.flat[w] + sg.flat : nullptr;
     }
 
+    // No early exit when no replica used the gradient: a branch on the mask
+    // ahead of the loads lets the compiler fetch the mask chain first and the
+    // segment chain only after it (two more round trips per tile). With every
+    // replica's range empty nothing is read; the stores are skipped.
     bool on[W];
+    bool write = true;
     if (USED) {
-        const uint64_t m = T.used[sg.param];
-        if (m == 0) return;   // no replica used this gradient: leave it untouched
+        write = m != 0;   // no replica used this gradient: leave it untouched
 #pragma unroll
         for (int k = 0; k < W; ++k) on[k] = slots.has(k) && ((m >> slot_replica(sg.chunk, k, nrep)) & 1);
     } else {
@@ -394,22 +452,23 @@ __global__ __launch_bounds__(kThreads) void reduce_fixed(KernelTables T, int32_t
     const int tid = int(threadIdx.x);
     if (sg.head >= 0) {
         if (sg.head + (tin + 1) * TILE <= sg.len)
-            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots);
+            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots, write);
         else if (sg.len - sg.head >= 4)
-            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots);
+            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots, write);
         if (tin == 0) {
             const int64_t body = (sg.len - sg.head) / 4 * 4;
             const int64_t tail = sg.len - sg.head - body;
-            if (tid < sg.head) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, tid, sc, slots);
+            if (tid < sg.head)
+                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, tid, sc, slots, write);
             if (tid >= 64 && tid < 64 + tail)
                 fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, sg.head + body + (tid - 64),
-                                                                      sc, slots);
+                                                                      sc, slots, write);
         }
         return;
     }
     for (int64_t j = tid; j < TILE; j += kThreads) {
         const int64_t e = tin * TILE + j;
-        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, e, sc, slots);
+        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, e, sc, slots, write);
     }
 }
 
@@ -423,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
     const int32_t tile = tile_begin + int32_t(blockIdx.x);
     const DeviceSeg sg = T.segs[T.tile_seg[tile]];
     const int64_t tin = int64_t(tile - sg.tile0);
-    const uint64_t m = used_mask(T, sg);
+    const uint64_t m = sg.used;   // all ones without unused detection
     if (m == 0) return;   // no replica used this gradient: leave it untouched
 
     if (sg.head >= 0) {
@@ -462,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
             }
         }
     }
-    scalar_parts<MODE, HOOK>(T, sg, tin, TILE, sc, W, rs != 0);
+    scalar_parts<MODE, HOOK>(T, sg, m, tin, TILE, sc, W, rs != 0);
 }
 
 // n: the replica count (at most W; below W only with PARTIAL).
@@ -471,7 +530,7 @@ hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_til
                         unsigned lds, hipStream_t st, int n)
 {
     const dim3 g(n_tiles), b(kThreads);
-    if (t.used) {
+    if (t.masked) {
         if (rs)
             hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true, PARTIAL>), g, b, lds, st, t, tile_begin, sc, n);
         else

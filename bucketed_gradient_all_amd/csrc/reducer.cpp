@@ -113,6 +113,7 @@ int build_segments(PlanView &pv, bool split_by_param)
         s.chunk = chunk;
         s.tile0 = int32_t(tiles);
         s.head = -1;
+        s.used = ~uint64_t(0);
         int64_t nt = (len + TILE - 1) / TILE;
         if (tiles + nt > std::numeric_limits<int32_t>::max()) return false;
         int32_t id = int32_t(pv.segs.size());
@@ -209,7 +210,7 @@ int validate(const ddp_reducer_desc *d, PlanView &pv)
 }
 
 struct Layout {
-    size_t grads_off = 0, flat_off = 0, segs_off = 0, tiles_off = 0, used_off = 0, total = 0;
+    size_t grads_off = 0, flat_off = 0, segs_off = 0, tiles_off = 0, total = 0;
 };
 
 Layout layout_of(const PlanView &pv)
@@ -224,8 +225,6 @@ Layout layout_of(const PlanView &pv)
     cur = align_up(cur + sizeof(DeviceSeg) * pv.segs.size());
     l.tiles_off = cur;
     cur = align_up(cur + sizeof(int32_t) * pv.tile_seg.size());
-    l.used_off = cur;
-    if (pv.find_unused) cur = align_up(cur + sizeof(uint64_t) * size_t(pv.P));
     l.total = cur;
     return l;
 }
@@ -272,10 +271,20 @@ struct ddp_reducer {
     bool window_set = false;
     std::vector<uint64_t> masks;          // [P] bit w: replica w contributes gradient p
     bool masks_uploaded = false;
-    uint64_t *stage = nullptr;            // pinned host staging, 2 slots of P masks
+    DeviceSeg *stage = nullptr;           // pinned host staging, 2 slots of the segment table
     hipEvent_t stage_ev[2] = {nullptr, nullptr};
     int stage_slot = 0;
-    uint64_t *used_dev = nullptr;         // device masks inside the workspace
+    DeviceSeg *segs_dev = nullptr;        // the segment table inside the workspace
+
+    // the segment table with each segment's mask (its gradient's); with
+    // unused detection every segment lies inside one gradient
+    void segment_records(DeviceSeg *out) const
+    {
+        for (size_t i = 0; i < pv.segs.size(); ++i) {
+            out[i] = pv.segs[i];
+            out[i].used = masks[size_t(pv.segs[i].param)];
+        }
+    }
     // per-iteration state [DDP-ch17 §17.12, §17.16]
     std::vector<int32_t> pending;
     // bucket groups [MegatronDDP §3]: group g = buckets [group_first[g],
@@ -423,14 +432,15 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
 // over replicas (a bitwise OR) [DDP-ch17 §17.33; PTD-notes §3.2].
 int upload_masks(ddp_reducer *r)
 {
-    if (!r->pv.find_unused || !r->device || r->masks_uploaded || r->pv.P == 0) return DDP_OK;
+    if (!r->pv.find_unused || !r->device || r->masks_uploaded || r->pv.segs.empty()) return DDP_OK;
     const int slot = r->stage_slot;
     r->stage_slot ^= 1;
     hipError_t e = hipEventSynchronize(r->stage_ev[slot]);   // the copy that last used this slot is done
     if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
-    uint64_t *h = r->stage + size_t(slot) * r->pv.P;
-    std::copy(r->masks.begin(), r->masks.end(), h);
-    e = hipMemcpyAsync(r->used_dev, h, sizeof(uint64_t) * r->pv.P, hipMemcpyHostToDevice, r->comm);
+    const size_t n = r->pv.segs.size();
+    DeviceSeg *h = r->stage + size_t(slot) * n;
+    r->segment_records(h);
+    e = hipMemcpyAsync(r->segs_dev, h, sizeof(DeviceSeg) * n, hipMemcpyHostToDevice, r->comm);
     if (e == hipSuccess) e = hipEventRecord(r->stage_ev[slot], r->comm);
     if (e != hipSuccess) return hip_fail("mask upload", e);
     r->masks_uploaded = true;
@@ -708,7 +718,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         std::memcpy(host.data() + lay.tiles_off, pv.tile_seg.data(), sizeof(int32_t) * pv.tile_seg.size());
         if (pv.find_unused) {
             r->compute_masks();   // nothing recorded yet: every replica contributes
-            std::memcpy(host.data() + lay.used_off, r->masks.data(), sizeof(uint64_t) * pv.P);
+            r->segment_records(reinterpret_cast<DeviceSeg *>(host.data() + lay.segs_off));
         }
         hipError_t e = hipMemcpy(desc->workspace, host.data(), lay.total, hipMemcpyHostToDevice);
         if (e != hipSuccess) {
@@ -718,13 +728,11 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         uint8_t *ws = static_cast<uint8_t *>(desc->workspace);
         r->tables.grads = copy_src ? reinterpret_cast<const void *const *>(ws + lay.grads_off) : nullptr;
         r->tables.flat = reinterpret_cast<float *const *>(ws + lay.flat_off);
-        r->tables.segs = reinterpret_cast<const DeviceSeg *>(ws + lay.segs_off);
+        r->segs_dev = reinterpret_cast<DeviceSeg *>(ws + lay.segs_off);
+        r->tables.segs = r->segs_dev;
         r->tables.tile_seg = reinterpret_cast<const int32_t *>(ws + lay.tiles_off);
         r->tables.n_params = pv.P;
-        if (pv.find_unused) {
-            r->used_dev = reinterpret_cast<uint64_t *>(ws + lay.used_off);
-            r->tables.used = r->used_dev;
-        }
+        r->tables.masked = pv.find_unused ? 1 : 0;
         int dev = 0;
         e = hipGetDevice(&dev);
         if (e == hipSuccess)
@@ -735,8 +743,8 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&r->ev_done, hipEventDisableTiming | hipEventDisableSystemFence);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_host, hipEventDisableTiming);
-        if (e == hipSuccess && pv.find_unused && pv.P > 0) {
-            e = hipHostMalloc(reinterpret_cast<void **>(&r->stage), 2 * sizeof(uint64_t) * pv.P);
+        if (e == hipSuccess && pv.find_unused && !pv.segs.empty()) {
+            e = hipHostMalloc(reinterpret_cast<void **>(&r->stage), 2 * sizeof(DeviceSeg) * pv.segs.size());
             for (int k = 0; k < 2 && e == hipSuccess; ++k)
                 e = hipEventCreateWithFlags(&r->stage_ev[k], hipEventDisableTiming);
         }

@@ -27,7 +27,9 @@
  * the pointer tables into its own host memory at creation and writes its
  * device tables into the caller's workspace; it allocates no device memory.
  * With unused-parameter detection it allocates one pinned host staging
- * buffer of 16 * P bytes (hipHostMalloc), freed by ddp_reducer_destroy.
+ * buffer (hipHostMalloc) of two copies of its segment table, 96 bytes per
+ * segment (a segment is the part of one gradient inside one ring chunk, so
+ * at most P + B * W of them), freed by ddp_reducer_destroy.
  *
  * Threading: a reducer is used from one thread at a time (hooks fire from
  * one thread, [DDP-ch17 §17.12]); that thread may change between calls, as
@@ -255,7 +257,9 @@ int ddp_set_require_sync(ddp_reducer *r, int32_t sync);
  *  - gradients no replica used are not written (their flat-buffer slices keep
  *    their contents).
  * The reduced tables go to the device once per synchronized backward, on the
- * comm stream, ahead of its first reduction. Without a call every replica
+ * comm stream, ahead of its first reduction, as a fresh copy of the segment
+ * table (48 bytes per segment, each record carrying its gradient's replica
+ * mask). Without a call every replica
  * counts as having used every gradient. Errors: DDP_ERR_INVALID if detection
  * is off or the backward already started. */
 int ddp_set_local_used(ddp_reducer *r, const uint8_t *used);

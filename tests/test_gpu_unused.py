@@ -7,7 +7,7 @@ import random
 import numpy as np
 import pytest
 
-from test_gpu_parity import Run, _small_workload, _torch, assert_bits, owned_mask, say
+from test_gpu_parity import INF, Run, _small_workload, _torch, assert_bits, owned_mask, say
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +77,40 @@ def test_unused_slices_are_zero_and_globally_unused_untouched(W, mode, collectiv
     order = [p for p in range(P - 1, -1, -1) if p not in unused_everywhere]
     for p in order:
         ddp.ddp_mark_ready(run.r, p)
+    ddp.ddp_finish(run.r, host_blocking=True)
+    check(run, used, before, collective)
+    run.close()
+
+
+@pytest.mark.parametrize("W,mode,collective", [(4, 0, 0), (8, 0, 0), (8, 2, 0), (12, 0, 1), (16, 1, 1), (16, 2, 0)])
+def test_unused_last_tiles_that_start_past_the_segment(W, mode, collective):
+    """Gradients of a tile plus four elements (for tiles of 1024, 2048 and
+    4096 elements), each behind a 4-element one, so that most start inside a
+    256-byte line: the vector body then starts a head of 4..60 elements late
+    and the gradient's second tile begins at or past its end. Both tiles take
+    the bounds-checked path, whose masked loads get an empty range for the
+    unused replicas and an offset past the range for the lanes outside the
+    segment. Twelve copies of each size, so that the W - 1 chunk boundaries
+    of the single bucket leave most of them whole."""
+    from synth.workloads import DIST_NORMAL, Workload
+    shapes = []
+    for _ in range(12):
+        for t in (1024, 2048, 4096):
+            shapes += [(4,), (t + 4,)]
+    wl = Workload(f"pastend_w{W}_m{mode}_c{collective}", shapes, world=W, cap_bytes=INF, first_cap_bytes=INF,
+                  dist=DIST_NORMAL, sigma=1.0, input_mode=mode, seed=4242 + W + 10 * mode)
+    P = len(wl.numel)
+    say(f"case unused past-end {wl.name} P={P}")
+    rng = random.Random(W * 31 + mode)
+    used = random_used(rng, W, P, p_unused=0.3, p_global=0.1)
+    run = URun(wl, collective)
+    before = [run.flat_host(w) for w in range(W)]
+    ddp = run.ddp
+    ddp.ddp_prepare_for_backward(run.r)
+    ddp.ddp_set_local_used(run.r, used)
+    for p in range(P - 1, -1, -1):
+        if any(used[w][p] for w in range(W)):
+            ddp.ddp_mark_ready(run.r, p)
     ddp.ddp_finish(run.r, host_blocking=True)
     check(run, used, before, collective)
     run.close()
