@@ -116,6 +116,33 @@ def test_unused_last_tiles_that_start_past_the_segment(W, mode, collective):
     run.close()
 
 
+@pytest.mark.parametrize("W,mode,collective", [(4, 0, 0), (8, 2, 1), (16, 0, 0), (16, 2, 0), (24, 0, 1), (32, 0, 0)])
+def test_unused_with_unaligned_sources_and_shifted_outputs(W, mode, collective):
+    """Unused masks on the one-element-per-lane paths: sources off their
+    16-byte alignment (every segment folded one element per lane) and flat
+    buffers shifted off their 256-byte phase (heads and tails on every
+    segment). A replica that did not use a gradient must still contribute +0
+    there, and gradients no replica used must stay untouched."""
+    cases = ((4 if mode == 0 else 2, 0), (0, 3), (0, [0, 4, 8, 12] * (W // 4) + [0] * (W % 4)))
+    for misalign, shift in cases:
+        wl = _small_workload(31000 + 100 * W + 10 * mode + collective, W, mode)
+        P = len(wl.numel)
+        say(f"case unused unaligned {wl.name} misalign={misalign} shift={shift} collective={collective}")
+        run = Run(wl, misalign=misalign, flat_shift=shift, collective=collective, find_unused=True)
+        used = random_used(random.Random(W + 7 * mode + collective), W, P, p_unused=0.3, p_global=0.15)
+        before = [run.flat_host(w) for w in range(W)]
+        ddp = run.ddp
+        ddp.ddp_prepare_for_backward(run.r)
+        ddp.ddp_set_local_used(run.r, used)
+        for p in range(P - 1, -1, -1):
+            if any(used[w][p] for w in range(W)):
+                ddp.ddp_mark_ready(run.r, p)
+        ddp.ddp_finish(run.r, host_blocking=True)
+        run.torch.cuda.synchronize()
+        check(run, used, before, collective)
+        run.close()
+
+
 def test_no_sync_accumulates_used_tables_and_reduces_once():
     """Two no_sync passes launch nothing; the synchronized pass reduces with
     the OR of the three passes' used tables."""
