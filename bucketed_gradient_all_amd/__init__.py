@@ -330,7 +330,10 @@ def ddp_set_require_sync(r: Reducer, sync: bool) -> None:
 
 def ddp_set_local_used(r: Reducer, used) -> None:
     """used: [W, P] (or flat W*P) array, nonzero = replica used the gradient."""
-    arr = np.ascontiguousarray(np.asarray(used) != 0, dtype=np.uint8).reshape(-1)
+    arr = np.asarray(used)
+    if arr.dtype != np.uint8:      # the library reads any nonzero byte as "used"
+        arr = (arr != 0).astype(np.uint8)
+    arr = np.ascontiguousarray(arr).reshape(-1)
     W, P = r.desc.c.world, r.desc.numel.size
     if arr.size != W * P:
         raise ValueError(f"used table must have {W}*{P} entries")

@@ -367,9 +367,14 @@ struct ddp_reducer {
         const uint64_t all = pv.W >= 64 ? ~uint64_t(0) : ((uint64_t(1) << pv.W) - 1);
         masks.assign(pv.P, window_set ? 0 : all);
         if (!window_set) return;
-        for (int w = 0; w < pv.W; ++w)
-            for (int32_t p = 0; p < pv.P; ++p)
-                if (window[size_t(w) * pv.P + p]) masks[p] |= uint64_t(1) << w;
+        // replica-major rows, one contiguous pass each (window entries are 0 or 1)
+        uint64_t *m = masks.data();
+        const int W = pv.W;
+        const int32_t P = pv.P;
+        for (int w = 0; w < W; ++w) {
+            const uint8_t *row = window.data() + size_t(w) * P;
+            for (int32_t p = 0; p < P; ++p) m[p] |= uint64_t(row[p]) << w;
+        }
     }
 };
 
@@ -890,8 +895,11 @@ int ddp_set_local_used(ddp_reducer *r, const uint8_t *used)
     if (!r->pv.find_unused) return fail(DDP_ERR_INVALID, "unused-parameter detection is off for this reducer");
     if (r->sync && r->marks > 0)
         return fail(DDP_ERR_INVALID, "the used table must be set before the first gradient of the backward");
-    for (size_t i = 0; i < r->window.size(); ++i)
-        if (used[i]) r->window[i] = 1;
+    // bounds in locals: a byte store may alias the vector's own pointers, so
+    // a loop on window.size() would reload them after every element
+    uint8_t *win = r->window.data();
+    const size_t n = r->window.size();
+    for (size_t i = 0; i < n; ++i) win[i] |= uint8_t(used[i] != 0);
     r->window_set = true;
     return DDP_OK;
 }
