@@ -275,6 +275,7 @@ struct ddp_reducer {
     hipEvent_t stage_ev[2] = {nullptr, nullptr};
     int stage_slot = 0;
     DeviceSeg *segs_dev = nullptr;        // the segment table inside the workspace
+    std::vector<uint64_t> device_masks;   // [P] the masks that table holds (its last upload)
 
     // the segment table with each segment's mask (its gradient's); with
     // unused detection every segment lies inside one gradient
@@ -434,10 +435,15 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
 // cross-stream event (a few microseconds of queue latency) is skipped.
 // The replica masks of this backward go to the device once, on the comm
 // stream, ahead of its first reduction: the per-replica "used" tables reduced
-// over replicas (a bitwise OR) [DDP-ch17 §17.33; PTD-notes §3.2].
+// over replicas (a bitwise OR) [DDP-ch17 §17.33; PTD-notes §3.2]. Masks equal
+// to those of the last upload are not sent again.
 int upload_masks(ddp_reducer *r)
 {
     if (!r->pv.find_unused || !r->device || r->masks_uploaded || r->pv.segs.empty()) return DDP_OK;
+    if (r->masks == r->device_masks) {   // the usual case: the same gradients unused as last time
+        r->masks_uploaded = true;
+        return DDP_OK;
+    }
     const int slot = r->stage_slot;
     r->stage_slot ^= 1;
     hipError_t e = hipEventSynchronize(r->stage_ev[slot]);   // the copy that last used this slot is done
@@ -448,6 +454,7 @@ int upload_masks(ddp_reducer *r)
     e = hipMemcpyAsync(r->segs_dev, h, sizeof(DeviceSeg) * n, hipMemcpyHostToDevice, r->comm);
     if (e == hipSuccess) e = hipEventRecord(r->stage_ev[slot], r->comm);
     if (e != hipSuccess) return hip_fail("mask upload", e);
+    r->device_masks = r->masks;
     r->masks_uploaded = true;
     return DDP_OK;
 }
@@ -724,6 +731,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
         if (pv.find_unused) {
             r->compute_masks();   // nothing recorded yet: every replica contributes
             r->segment_records(reinterpret_cast<DeviceSeg *>(host.data() + lay.segs_off));
+            r->device_masks = r->masks;
         }
         hipError_t e = hipMemcpy(desc->workspace, host.data(), lay.total, hipMemcpyHostToDevice);
         if (e != hipSuccess) {

@@ -259,7 +259,8 @@ int ddp_set_require_sync(ddp_reducer *r, int32_t sync);
  * The reduced tables go to the device once per synchronized backward, on the
  * comm stream, ahead of its first reduction, as a fresh copy of the segment
  * table (48 bytes per segment, each record carrying its gradient's replica
- * mask). Without a call every replica
+ * mask), unless the masks equal those the device already holds. Without a
+ * call every replica
  * counts as having used every gradient. Errors: DDP_ERR_INVALID if detection
  * is off or the backward already started. */
 int ddp_set_local_used(ddp_reducer *r, const uint8_t *used);

@@ -143,6 +143,35 @@ def test_unused_with_unaligned_sources_and_shifted_outputs(W, mode, collective):
         run.close()
 
 
+def test_repeated_and_changed_masks_across_backwards():
+    """The masked segment table is sent to the device only when the masks
+    differ from what it holds: tables A, A, B, A, all-used over five
+    synchronized backwards, each result bit-exact against the oracle."""
+    W, mode = 8, 0
+    wl = _small_workload(5150, W, mode)
+    P = len(wl.numel)
+    rng = random.Random(5150)
+    a = random_used(rng, W, P, p_unused=0.3, p_global=0.2)
+    b = random_used(rng, W, P, p_unused=0.3, p_global=0.2)
+    every = [[1] * P for _ in range(W)]
+    say(f"case repeated masks {wl.name} P={P}")
+    run = URun(wl, 0)
+    ddp = run.ddp
+    for k, used in enumerate((a, a, b, a, every)):
+        run.inputs.refill()
+        before = [run.flat_host(w) for w in range(W)]
+        ddp.ddp_prepare_for_backward(run.r)
+        ddp.ddp_set_local_used(run.r, used)
+        for p in range(P - 1, -1, -1):
+            if any(used[w][p] for w in range(W)):
+                ddp.ddp_mark_ready(run.r, p)
+        ddp.ddp_finish(run.r, host_blocking=True)
+        run.torch.cuda.synchronize()
+        say(f"  backward {k}")
+        check(run, used, before)
+    run.close()
+
+
 def test_no_sync_accumulates_used_tables_and_reduces_once():
     """Two no_sync passes launch nothing; the synchronized pass reduces with
     the OR of the three passes' used tables."""
