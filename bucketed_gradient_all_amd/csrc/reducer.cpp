@@ -451,6 +451,7 @@ int upload_masks(ddp_reducer *r)
     const size_t n = r->pv.segs.size();
     DeviceSeg *h = r->stage + size_t(slot) * n;
     r->segment_records(h);
+    r->device_masks.clear();   // unknown from here until the copy is queued: a failure forces a new upload
     e = hipMemcpyAsync(r->segs_dev, h, sizeof(DeviceSeg) * n, hipMemcpyHostToDevice, r->comm);
     if (e == hipSuccess) e = hipEventRecord(r->stage_ev[slot], r->comm);
     if (e != hipSuccess) return hip_fail("mask upload", e);

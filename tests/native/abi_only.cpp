@@ -7,7 +7,13 @@
 // (W + 1) / 2 * m / 64. That closed form is the check here; the bit-exact
 // comparison against the CPU oracle is the Python tests' job.
 //
-// usage: abi_only W collective     (W a power of two, collective 0 or 1)
+// With unused-parameter detection (third argument 1) replica w uses gradient
+// p unless (w + p) % 3 == 0, and gradient 2 is used by no replica. A used
+// gradient's value is then S_p * m / (64 W), S_p the sum of w + 1 over the
+// replicas that used it (the others contribute zeros), still exact; gradient
+// 2's flat slice must keep its contents.
+//
+// usage: abi_only W collective [unused]   (W a power of two, collective 0 or 1)
 // exit status 0 when every element of every replica matches.
 #include "ddp.h"
 
@@ -16,6 +22,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #define HIP_OK(x)                                                                       \
@@ -45,10 +52,12 @@ int main(int argc, char **argv)
 {
     const int W = argc > 1 ? std::atoi(argv[1]) : 8;
     const int collective = argc > 2 ? std::atoi(argv[2]) : DDP_ALL_REDUCE;
+    const int unused = argc > 3 ? std::atoi(argv[3]) : 0;
     if (W < 1 || (W & (W - 1)) != 0 || W > 64) {
         std::fprintf(stderr, "W must be a power of two up to 64\n");
         return 2;
     }
+    const int32_t kUnusedEverywhere = 2;
     // gradient sizes in elements, in registration order: odd sizes, a
     // zero-size gradient and one larger than a tile
     const std::vector<int64_t> numel = {1000, 4096, 77, 0, 100003, 3, 65536, 1};
@@ -99,7 +108,7 @@ int main(int argc, char **argv)
     d.compute_stream = compute;
     d.comm_stream = comm;
     d.collective = collective;
-    d.find_unused = 0;
+    d.find_unused = unused;
     d.workspace_bytes = ddp_workspace_bytes(&d);
     if (d.workspace_bytes == 0) {
         std::fprintf(stderr, "ddp_workspace_bytes: %s\n", ddp_last_error());
@@ -109,18 +118,34 @@ int main(int argc, char **argv)
     ddp_reducer *r = nullptr;
     DDP_OK_(ddp_reducer_create(&d, &r));
 
-    std::vector<int32_t> order(P);
-    for (int i = 0; i < P; ++i) order[i] = P - 1 - i;
+    // used[w * P + p]: replica w produced gradient p (unused detection only)
+    std::vector<uint8_t> used(size_t(W) * P, 1);
+    std::vector<int64_t> used_sum(P, int64_t(W) * (W + 1) / 2);   // S_p: sum of w + 1 over users
+    if (unused) {
+        for (int p = 0; p < P; ++p) {
+            used_sum[p] = 0;
+            for (int w = 0; w < W; ++w) {
+                const bool u = p != kUnusedEverywhere && (w + p) % 3 != 0;
+                used[size_t(w) * P + p] = u;
+                if (u) used_sum[p] += w + 1;
+            }
+        }
+    }
+    std::vector<int32_t> order;   // gradients someone used, in reverse registration order
+    for (int i = P - 1; i >= 0; --i)
+        if (used_sum[i] > 0) order.push_back(i);
+    const int32_t n_marks = int32_t(order.size());
     int64_t bad = 0;
     for (int iter = 0; iter < 2; ++iter) {
         DDP_OK_(ddp_prepare_for_backward(r));
+        if (unused) DDP_OK_(ddp_set_local_used(r, used.data()));
         int32_t done = 0;
-        DDP_OK_(ddp_mark_ready_many(r, order.data(), P, &done));
+        DDP_OK_(ddp_mark_ready_many(r, order.data(), n_marks, &done));
         DDP_OK_(ddp_finish(r, 1));
         int32_t launched = 0;
         DDP_OK_(ddp_get_launched(r, &launched));
-        if (done != P || launched != B) {
-            std::fprintf(stderr, "marked %d of %d, launched %d of %d buckets\n", done, P, launched, B);
+        if (done != n_marks || launched != B) {
+            std::fprintf(stderr, "marked %d of %d, launched %d of %d buckets\n", done, n_marks, launched, B);
             return 1;
         }
         for (int w = 0; w < W; ++w) {
@@ -134,7 +159,15 @@ int main(int argc, char **argv)
                     const int64_t e = offset[p] / 4 + i;   // element of the bucket
                     const bool owned = collective == DDP_ALL_REDUCE || e / q == w;
                     if (!owned) continue;                    // another replica's shard: never written
-                    const float want = float(W + 1) / 2.0f * float(i % 7 + 1) / 64.0f;
+                    if (used_sum[p] == 0) {                  // used by no replica: never written
+                        uint32_t bits;
+                        std::memcpy(&bits, &got[base + i], 4);
+                        if (bits != 0xFFFFFFFFu && bad++ < 5)
+                            std::fprintf(stderr, "replica %d unused gradient %d element %lld was written\n", w,
+                                         p, (long long)i);
+                        continue;
+                    }
+                    const float want = float(used_sum[p]) * float(i % 7 + 1) / (64.0f * float(W));
                     if (got[base + i] != want && bad++ < 5)
                         std::fprintf(stderr, "replica %d gradient %d element %lld: %g, want %g\n", w, p,
                                      (long long)i, double(got[base + i]), double(want));
@@ -153,7 +186,7 @@ int main(int argc, char **argv)
         std::fprintf(stderr, "%lld mismatches\n", (long long)bad);
         return 1;
     }
-    std::printf("abi_only ok: W=%d collective=%d, %d gradients, %d buckets, %lld elements, 2 iterations\n", W,
-                collective, P, B, (long long)total);
+    std::printf("abi_only ok: W=%d collective=%d unused=%d, %d gradients, %d buckets, %lld elements, 2 iterations\n",
+                W, collective, unused, P, B, (long long)total);
     return 0;
 }
