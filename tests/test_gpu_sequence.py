@@ -51,26 +51,35 @@ def _expected(run, grads, window, before):
     return out
 
 
-def _write_grads(run, grads):
+def _write_grads(run, grads, view):
+    """The accumulated gradients into the reducer's inputs: the per-gradient
+    buffers (copy mode) or the flat buffers themselves (view mode, where each
+    gradient is a view of its bucket slot)."""
     torch = _torch()
-    inp = run.inputs
+    inp, plan = run.inputs, run.plan
     for w in range(run.wl.world):
         for p, n in enumerate(run.wl.numel):
             if n == 0:
                 continue
-            off = inp.grad_off[p]
-            dst = inp.grads[w][off:off + 4 * n].view(torch.float32)
+            if view:
+                o = run.bucket_flat[plan.bucket_of[p]] + int(plan.offset_in_bucket[p]) // 4
+                dst = inp.flat[w][o:o + n]
+            else:
+                off = inp.grad_off[p]
+                dst = inp.grads[w][off:off + 4 * n].view(torch.float32)
             dst.copy_(torch.from_numpy(grads[w][p]))
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("W,collective,seed", [(6, 0, 1), (8, 1, 2), (16, 0, 3), (3, 0, 4)])
-def test_long_training_loop_with_no_sync_windows(W, collective, seed):
+@pytest.mark.parametrize("W,collective,mode,seed", [(6, 0, 0, 1), (8, 1, 0, 2), (16, 0, 0, 3), (3, 0, 0, 4),
+                                                   (8, 0, 1, 5), (12, 1, 1, 6)])
+def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
     rng = random.Random(seed)
     nprng = np.random.default_rng(seed)
-    wl = _small_workload(70000 + seed, W, 0)
+    wl = _small_workload(70000 + seed, W, mode)
+    view = mode == 1
     P = len(wl.numel)
-    say(f"case sequence W={W} collective={collective} P={P} cap={wl.cap_bytes}")
+    say(f"case sequence W={W} collective={collective} mode={mode} P={P} cap={wl.cap_bytes}")
     run = Run(wl, collective=collective, find_unused=True)
     ddp = run.ddp
     B = run.plan.n_buckets
@@ -90,7 +99,7 @@ def test_long_training_loop_with_no_sync_windows(W, collective, seed):
         for w in range(W):
             for p, n in enumerate(wl.numel):
                 grads[w][p] = grads[w][p] + nprng.standard_normal(n).astype(np.float32)
-        _write_grads(run, grads)
+        _write_grads(run, grads, view)
         if rng.random() < 0.4:
             used = last_used                       # the same branches as last time
         else:
