@@ -468,6 +468,9 @@ def main():
               "so runs on more than one GPU are not part of this benchmark (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    import __graft_entry__
+    __graft_entry__.ensure_built()   # a fresh checkout builds once; a built tree is used as it is
+
     import torch
     import synth
     from synth import workloads as wls
