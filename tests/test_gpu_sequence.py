@@ -18,11 +18,12 @@ from test_gpu_parity import Run, _small_workload, _torch, assert_bits, owned_mas
 pytestmark = pytest.mark.gpu
 
 
-def _expected(run, grads, window, before):
+def _expected(run, grads, window, before, wgrads=None):
     """Per replica: the flat buffer the synchronized backward should leave.
     Each bucket is folded by the oracle over replicas whose slice of a
-    gradient is its accumulated gradient if the replica used it in the window
-    and zeros otherwise; gradients no replica used keep `before`."""
+    gradient is its accumulated gradient (bf16 mode: its main_grad and this
+    backward's wgrad) if the replica used it in the window and zeros
+    otherwise; gradients no replica used keep `before`."""
     from oracle import fold
     wl, plan = run.wl, run.plan
     W, numel = wl.world, wl.numel
@@ -32,15 +33,19 @@ def _expected(run, grads, window, before):
         n = int(plan.bucket_bytes[b]) // 4
         if n == 0:
             continue
-        xs = []
+        xs, gs = [], []
         for w in range(W):
             x = np.zeros(n, np.float32)
+            g = np.zeros(n, np.uint16)
             for p in members:
                 if window[w][p]:
                     o = int(plan.offset_in_bucket[p]) // 4
                     x[o:o + numel[p]] = grads[w][p]
+                    if wgrads is not None:
+                        g[o:o + numel[p]] = wgrads[w][p]
             xs.append(x)
-        red = fold.reduce_f32(xs)
+            gs.append(g)
+        red = fold.reduce_f32(xs) if wgrads is None else fold.reduce_bf16acc(xs, gs)
         base = run.bucket_flat[b]
         for p in members:
             if not any(window[w][p] for w in range(W)):
@@ -51,33 +56,44 @@ def _expected(run, grads, window, before):
     return out
 
 
-def _write_grads(run, grads, view):
+def _write_grads(run, grads, mode, wgrads=None):
     """The accumulated gradients into the reducer's inputs: the per-gradient
     buffers (copy mode) or the flat buffers themselves (view mode, where each
-    gradient is a view of its bucket slot)."""
+    gradient is a view of its bucket slot; bf16 mode, where the flat buffer
+    is main_grad and the per-gradient buffers hold bf16 wgrads)."""
     torch = _torch()
     inp, plan = run.inputs, run.plan
     for w in range(run.wl.world):
         for p, n in enumerate(run.wl.numel):
             if n == 0:
                 continue
-            if view:
+            if mode in (1, 2):
                 o = run.bucket_flat[plan.bucket_of[p]] + int(plan.offset_in_bucket[p]) // 4
-                dst = inp.flat[w][o:o + n]
+                inp.flat[w][o:o + n].copy_(torch.from_numpy(grads[w][p]))
             else:
                 off = inp.grad_off[p]
-                dst = inp.grads[w][off:off + 4 * n].view(torch.float32)
-            dst.copy_(torch.from_numpy(grads[w][p]))
+                inp.grads[w][off:off + 4 * n].view(torch.float32).copy_(torch.from_numpy(grads[w][p]))
+            if mode == 2:
+                off = inp.grad_off[p]
+                inp.grads[w][off:off + 2 * n].view(torch.int16).copy_(torch.from_numpy(wgrads[w][p].view(np.int16)))
     torch.cuda.synchronize()
 
 
+def _bf16_bits(x):
+    """bf16 bit patterns of fp32 values (the upper half, truncated)."""
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _widen(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
 @pytest.mark.parametrize("W,collective,mode,seed", [(6, 0, 0, 1), (8, 1, 0, 2), (16, 0, 0, 3), (3, 0, 0, 4),
-                                                   (8, 0, 1, 5), (12, 1, 1, 6)])
+                                                   (8, 0, 1, 5), (12, 1, 1, 6), (16, 0, 2, 7), (8, 1, 2, 8)])
 def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
     rng = random.Random(seed)
     nprng = np.random.default_rng(seed)
     wl = _small_workload(70000 + seed, W, mode)
-    view = mode == 1
     P = len(wl.numel)
     say(f"case sequence W={W} collective={collective} mode={mode} P={P} cap={wl.cap_bytes}")
     run = Run(wl, collective=collective, find_unused=True)
@@ -95,11 +111,22 @@ def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
         ddp.ddp_set_require_sync(run.r, sync)
         if B > 1 and rng.random() < 0.3:
             ddp.ddp_set_bucket_groups(run.r, [0] + sorted(rng.sample(range(1, B), rng.randint(0, B - 1))))
-        # this backward's gradients, added to what the window accumulated so far
-        for w in range(W):
-            for p, n in enumerate(wl.numel):
-                grads[w][p] = grads[w][p] + nprng.standard_normal(n).astype(np.float32)
-        _write_grads(run, grads, view)
+        # this backward's gradients, added to what the window accumulated so
+        # far. In bf16 mode a no_sync backward's wgrad is folded into
+        # main_grad by the caller (gradient accumulation); the synchronized
+        # backward's wgrad is added by the reduction itself.
+        wgrads = None
+        if mode == 2:
+            wgrads = [[_bf16_bits(nprng.standard_normal(n)) for n in wl.numel] for _ in range(W)]
+            if not sync:
+                for w in range(W):
+                    for p in range(P):
+                        grads[w][p] = grads[w][p] + _widen(wgrads[w][p])
+        else:
+            for w in range(W):
+                for p, n in enumerate(wl.numel):
+                    grads[w][p] = grads[w][p] + nprng.standard_normal(n).astype(np.float32)
+        _write_grads(run, grads, mode, wgrads)
         if rng.random() < 0.4:
             used = last_used                       # the same branches as last time
         else:
@@ -141,7 +168,7 @@ def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
         seen["unused_everywhere"] += any(not any(window[w][p] for w in range(W)) for p in range(P))
         seen["repeated_masks"] += prev_sync_masks == window
         prev_sync_masks = [row[:] for row in window]
-        want = _expected(run, grads, window, before)
+        want = _expected(run, grads, window, before, wgrads)
         for w in range(W):
             got = run.flat_host(w)
             m = owned_mask(run, w) if collective else np.ones(run.total, dtype=bool)
