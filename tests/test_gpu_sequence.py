@@ -3,7 +3,8 @@ it. No_sync windows leave gradients to accumulate in the caller's buffers and
 OR their used tables together; the next synchronized backward reduces the
 accumulated sum under the window's masks [L15 §4.1; PTD-notes §2.2.3,
 §2.2.4; DDP-ch17 §17.33]. Used tables repeat or change from one window to
-the next, bucket groups are regrouped between backwards [MegatronDDP §3],
+the next, bucket groups are regrouped and the built-in hook changed between
+backwards [MegatronDDP §3; DDP-ch17 §17.9],
 and gradients are marked in random orders and batches. Every synchronized
 backward is compared bit for bit with the oracle's fold of the accumulated
 gradients; gradients no replica used in the window must keep their
@@ -18,13 +19,13 @@ from test_gpu_parity import Run, _small_workload, _torch, assert_bits, owned_mas
 pytestmark = pytest.mark.gpu
 
 
-def _expected(run, grads, window, before, wgrads=None):
+def _expected(run, grads, window, before, wgrads=None, hook=0):
     """Per replica: the flat buffer the synchronized backward should leave.
     Each bucket is folded by the oracle over replicas whose slice of a
     gradient is its accumulated gradient (bf16 mode: its main_grad and this
     backward's wgrad) if the replica used it in the window and zeros
     otherwise; gradients no replica used keep `before`."""
-    from oracle import fold
+    from oracle import compress, fold
     wl, plan = run.wl, run.plan
     W, numel = wl.world, wl.numel
     out = [b.copy() for b in before]
@@ -45,7 +46,11 @@ def _expected(run, grads, window, before, wgrads=None):
                         g[o:o + numel[p]] = wgrads[w][p]
             xs.append(x)
             gs.append(g)
-        red = fold.reduce_f32(xs) if wgrads is None else fold.reduce_bf16acc(xs, gs)
+        if hook:
+            fmt = {1: compress.BF16, 2: compress.FP16}[hook]
+            red = compress.compressed_reduce(fmt, xs, gs if wgrads is not None else None)
+        else:
+            red = fold.reduce_f32(xs) if wgrads is None else fold.reduce_bf16acc(xs, gs)
         base = run.bucket_flat[b]
         for p in members:
             if not any(window[w][p] for w in range(W)):
@@ -106,9 +111,13 @@ def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
     seen = {"after_no_sync": 0, "masked_slice": 0, "unused_everywhere": 0, "repeated_masks": 0}
     passes_in_window = 0
     prev_sync_masks = None
+    hook, hooks_seen = 0, set()
     for it in range(24):
         sync = rng.random() < 0.6 or it == 23
         ddp.ddp_set_require_sync(run.r, sync)
+        if rng.random() < 0.3:   # the built-in hook may change between backwards
+            hook = rng.choice([0, 1, 2])
+            ddp.ddp_register_builtin_hook(run.r, hook)
         if B > 1 and rng.random() < 0.3:
             ddp.ddp_set_bucket_groups(run.r, [0] + sorted(rng.sample(range(1, B), rng.randint(0, B - 1))))
         # this backward's gradients, added to what the window accumulated so
@@ -168,7 +177,8 @@ def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
         seen["unused_everywhere"] += any(not any(window[w][p] for w in range(W)) for p in range(P))
         seen["repeated_masks"] += prev_sync_masks == window
         prev_sync_masks = [row[:] for row in window]
-        want = _expected(run, grads, window, before, wgrads)
+        hooks_seen.add(hook)
+        want = _expected(run, grads, window, before, wgrads, hook)
         for w in range(W):
             got = run.flat_host(w)
             m = owned_mask(run, w) if collective else np.ones(run.total, dtype=bool)
@@ -178,7 +188,8 @@ def test_long_training_loop_with_no_sync_windows(W, collective, mode, seed):
         grads = [[np.zeros(n, np.float32) for n in wl.numel] for _ in range(W)]
         window = [[0] * P for _ in range(W)]
         passes_in_window = 0
-    say(f"  {syncs} synchronized backwards; {seen}")
+    say(f"  {syncs} synchronized backwards; {seen}; hooks {sorted(hooks_seen)}")
     assert syncs >= 5
     assert all(seen.values()), seen
+    assert len(hooks_seen) >= 2, hooks_seen
     run.close()
