@@ -139,6 +139,7 @@ constexpr bool writes_through(int W, bool rs, bool partial)
 {
     return !rs && !partial && (W == 8 || W == 16);
 }
+static_assert(!writes_through(16, false, true), "partial instances keep their global stores");
 
 __device__ __forceinline__ void st4(float *p, f32x4 v)
 {
@@ -407,6 +408,7 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
         const uint32_t range = write ? 4 * span : 0;
 #pragma unroll
         for (int w = 0; w < NOUT; ++w) {
+            if (!(NOUT == 1 || slots.has(w))) continue;   // an absent slot has no destination
             const __amdgpu_buffer_rsrc_t rd = range_of(ds[w] + t0, range);
 #pragma unroll
             for (int u = 0; u < U; ++u) st4_in(rd, 4 * rel[u], acc[u]);
