@@ -132,12 +132,13 @@ __device__ __forceinline__ void st4_in(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(byte_off), 0, kStoreThrough);
 }
 
-// The instances that store through the L2 (all-reduce at 8 and 16 replicas;
-// measured: +1.5-4% for ResNet-50 and BERT-large, +2% for the W = 16 sweep;
-// not kept where it lost, as for the reduce-scatter and W = 4).
+// The instances that store through the L2 (all-reduce at 8, 16 and 32
+// replicas; measured: +1.5-4% for ResNet-50 and BERT-large, +2% for the
+// W = 16 and W = 32 sweeps; not kept where it lost, as for the reduce-scatter
+// and W = 4).
 constexpr bool writes_through(int W, bool rs, bool partial)
 {
-    return !rs && !partial && (W == 8 || W == 16);
+    return !rs && !partial && (W == 8 || W == 16 || W == 32);
 }
 static_assert(!writes_through(16, false, true), "partial instances keep their global stores");
 
