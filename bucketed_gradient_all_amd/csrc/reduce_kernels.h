@@ -334,7 +334,9 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // replica's source: a replica that did not use the gradient gets range 0,
 // so its loads return the zero-filled slice its term is defined by (a +0
 // input) and read nothing, with no branch; an out-of-range lane of the last
-// tile gets an offset past every range and reads nothing either.
+// tile gets an offset past every range and reads nothing either. The
+// instances that write through the L2 store the same way, over this tile of
+// each destination.
 template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED, bool PARTIAL>
 __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
                                             float *const (&ds)[NOUT], uint64_t on, const DeviceSeg &sg,
@@ -347,7 +349,7 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
     const int tid = int(threadIdx.x);
     const int64_t t0 = sg.head + tin * TILE;   // the tile's first element
     int64_t e[U], el[U];
-    uint32_t rel[U];   // element offset from t0 (USED loads)
+    uint32_t rel[U];   // element offset from t0 (buffer loads and stores)
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
