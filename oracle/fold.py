@@ -131,7 +131,3 @@ def reduce_scatter_f32(x: Sequence[np.ndarray]):
     full = reduce_f32(x)
     return [(lo, hi, full[lo:hi]) for lo, hi in chunk_bounds(full.size, len(x))]
 
-
-def reduce_scatter_bf16acc(main: Sequence[np.ndarray], wgrad: Sequence[np.ndarray]):
-    full = reduce_bf16acc(main, wgrad)
-    return [(lo, hi, full[lo:hi]) for lo, hi in chunk_bounds(full.size, len(main))]

@@ -263,3 +263,45 @@ def test_three_accumulation_schedules_agree_on_a_dyadic_grid():
     local = [sum(mb[k][w].astype(np.float64) for k in range(micro)).astype(np.float32) for w in range(W)]
     once = f.reduce_f32(local).astype(np.float64)
     np.testing.assert_array_equal(each, once)
+
+
+def test_three_replicas_at_flt_max_stay_finite():
+    """Pre-scaling on load [reading 7] keeps the mean of three largest
+    finite values finite: fp32(1/3) = (1 + 2^-25) / 3 is above 1/3, but
+    fl(FLT_MAX * fp32(1/3)) rounds down (to 0x7EAAAAAA) and the three terms
+    sum to exactly FLT_MAX. Summing first and scaling after would overflow
+    to inf. Worked here in numpy's own fp32 scalars, independently of the
+    oracle; the same holds for the negated inputs."""
+    fmax = np.float32(np.finfo(np.float32).max)
+    s = np.float32(1.0) / np.float32(3.0)
+    assert int(s.view(np.uint32)) == 0x3EAAAAAB and 3 * 11184811 == 2 ** 25 + 1
+    t = np.float32(fmax * s)
+    assert int(t.view(np.uint32)) == 0x7EAAAAAA
+    assert np.float32(np.float32(t + t) + t) == fmax
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(np.float32(fmax + fmax) + fmax) * s)   # sum first: inf
+    out = _fold().reduce_f32([np.full(5, fmax, np.float32)] * 3)
+    assert np.all(out == fmax)
+    out = _fold().reduce_f32([np.full(5, -fmax, np.float32)] * 3)
+    assert np.all(out == -fmax)
+
+
+def test_subnormal_terms_and_sums_are_kept():
+    """No flush to zero [reading 9]: subnormal inputs scale and add as IEEE
+    fp32 does. W = 2 with the smallest subnormal on both replicas: each term
+    fl(2^-149 * 0.5) rounds to even, i.e. to 0 (a tie), so the mean is +0;
+    with 3 * 2^-149 each term is 1.5 * 2^-149, which rounds to even 2^-148,
+    and the sum is 2^-147 (= 4 * 2^-149), a subnormal."""
+    tiny = np.uint32(1).view(np.float32)
+    out = _fold().reduce_f32([np.full(3, tiny, np.float32)] * 2)
+    assert np.all(out.view(np.uint32) == 0)
+    three = np.uint32(3).view(np.float32)
+    out = _fold().reduce_f32([np.full(3, three, np.float32)] * 2)
+    assert np.all(out.view(np.uint32) == 4)
+    # the largest subnormal on 4 replicas: terms 2^-2 * (2^23 - 1) * 2^-149 are exact
+    # only up to rounding; the sum of the four rounded terms is checked in exact arithmetic
+    big = np.uint32(0x007FFFFF).view(np.float32)
+    out = _fold().reduce_f32([np.full(2, big, np.float32)] * 4)
+    k = 0x007FFFFF
+    term = round(k / 4) if (k % 4) != 2 else (k // 4 if (k // 4) % 2 == 0 else k // 4 + 1)
+    assert int(out.view(np.uint32)[0]) == 4 * term
