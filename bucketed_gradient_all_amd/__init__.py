@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import weakref
 from typing import Callable, List, NamedTuple, Optional, Sequence
 
 import numpy as np
@@ -28,6 +29,7 @@ DDP_ERR_NOT_READY = -4
 DDP_ERR_ORDER = -5
 DDP_ERR_HIP = -6
 DDP_ERR_HOOK = -7
+DDP_ERR_NOMEM = -8
 
 DDP_ORDER_REVERSE = 0
 DDP_ORDER_GIVEN = 1
@@ -273,14 +275,36 @@ def ddp_workspace_bytes(desc: Desc) -> int:
     return int(n)
 
 
+def _release(holder: list, keep) -> None:
+    """Finalizer of a Reducer dropped without ddp_reducer_destroy: destroys
+    the native reducer (which waits for its comm stream) while `keep` (the
+    workspace and host tables it reads) is still referenced, so nothing the
+    queued reductions use goes back to an allocator first."""
+    h, holder[0] = holder[0], None
+    if h:
+        lib().ddp_reducer_destroy(h)
+
+
 class Reducer:
     """Handle of a ddp_reducer plus the objects it must keep alive."""
 
     def __init__(self, handle: int, desc: Desc):
-        self.handle = handle
+        self._holder = [handle]
         self.desc = desc
         self._hook = None
         self._hook_error: Optional[BaseException] = None
+        self.workspace = None
+        self._finalizer = weakref.finalize(self, _release, self._holder, [desc])
+
+    @property
+    def handle(self):
+        return self._holder[0]
+
+    def keep_alive(self, obj) -> None:
+        """Keeps obj (e.g. the device workspace) referenced until the native
+        reducer is destroyed, explicitly or by the finalizer."""
+        self._finalizer.detach()
+        self._finalizer = weakref.finalize(self, _release, self._holder, [self.desc, obj])
 
     def check(self, rc: int) -> int:
         """_check for calls that may run the Python hook: an exception the
@@ -298,9 +322,11 @@ def ddp_reducer_create(desc: Desc) -> Reducer:
 
 
 def ddp_reducer_destroy(r: Reducer) -> None:
-    if r.handle:
-        _check(lib().ddp_reducer_destroy(r.handle))
-        r.handle = None
+    h = r.handle
+    if h:
+        r._holder[0] = None
+        r._finalizer.detach()
+        _check(lib().ddp_reducer_destroy(h))
 
 
 def ddp_prepare_for_backward(r: Reducer) -> None:
@@ -458,4 +484,5 @@ def make_reducer(world: int, param_numel: Sequence[int], plan: BucketPlan, input
     desc.set_workspace(ws.data_ptr(), nbytes)
     r = ddp_reducer_create(desc)
     r.workspace = ws
+    r.keep_alive(ws)   # released only after the native reducer, which waits for its reductions
     return r

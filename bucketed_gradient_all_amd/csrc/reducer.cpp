@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <memory>
 #include <new>
 #include <string>
 #include <vector>
@@ -20,18 +21,61 @@ using ddp::KernelTables;
 
 namespace {
 
+// Text of the last error on this thread. Recording it never throws: when
+// the text cannot be stored (out of host memory), g_err_fixed points to a
+// static text instead.
 thread_local std::string g_err;
+thread_local const char *g_err_fixed = nullptr;
+constexpr const char *kNoMemText = "out of host memory";
 
-int fail(int code, const std::string &msg)
+int fail(int code, const std::string &msg) noexcept
 {
-    g_err = msg;
+    try {
+        g_err.assign(msg);
+        g_err_fixed = nullptr;
+    } catch (...) {
+        g_err_fixed = kNoMemText;
+    }
     return code;
 }
 
-int hip_fail(const char *what, hipError_t e)
+int fail(int code, const char *msg) noexcept
 {
-    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    try {
+        g_err.assign(msg);
+        g_err_fixed = nullptr;
+    } catch (...) {
+        g_err_fixed = kNoMemText;
+    }
+    return code;
+}
+
+int hip_fail(const char *what, hipError_t e) noexcept
+{
+    try {
+        g_err.assign(what);
+        g_err.append(": ");
+        g_err.append(hipGetErrorString(e));
+        g_err_fixed = nullptr;
+    } catch (...) {
+        g_err_fixed = kNoMemText;
+    }
     return DDP_ERR_HIP;
+}
+
+// Every entry point runs its body through this: the C ABI never lets an
+// exception out. Host memory exhaustion (std::bad_alloc from a container or
+// a message) becomes DDP_ERR_NOMEM; anything else DDP_ERR_INVALID.
+template <class F>
+int guarded(F &&body) noexcept
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return fail(DDP_ERR_NOMEM, kNoMemText);
+    } catch (...) {
+        return fail(DDP_ERR_INVALID, "internal error: unexpected exception in the host library");
+    }
 }
 
 std::string list_params(const std::vector<int32_t> &ps)
@@ -71,6 +115,10 @@ constexpr int auto_workgroups_per_cu(int W, bool reduce_scatter, bool bf16_accum
 }
 
 constexpr size_t kAlign = 256;
+
+// Event pairs in a reducer's timing ring (its only HIP events besides the
+// three stream-ordering ones and the two staging ones).
+constexpr int kTimingSlots = 256;
 
 size_t align_up(size_t x)
 {
@@ -258,10 +306,21 @@ struct ddp_reducer {
     // ev_ready keeps the default system-scope release: with device scope the
     // HIP runtime made every launch of a many-launch step about 20 us slower.
     hipEvent_t ev_ready = nullptr, ev_done = nullptr, ev_host = nullptr;
+    // unused detection: ev_tables orders a reduction on another stream after
+    // the segment-table upload on the comm stream; ev_foreign orders later
+    // uploads after that reduction
+    hipEvent_t ev_tables = nullptr, ev_foreign = nullptr;
+    // per-launch timing: a fixed ring of event pairs. Record i uses pair
+    // i mod kTimingSlots; before a pair is recorded again, the launch that
+    // last used it is waited for and its duration copied to the host record.
     bool timing = false;
-    std::vector<hipEvent_t> t0, t1;       // event pool, reused across record lists
-    std::vector<int32_t> timed_bucket;    // first bucket of each recorded launch
-    std::vector<int32_t> timed_count;     // buckets covered by each recorded launch
+    struct TimingRec {
+        int32_t first, count;   // first bucket of the launch, buckets it covered
+        float ms;               // kernel duration; read from the events once resolved
+    };
+    mutable std::vector<TimingRec> timed;   // launches since timing was last enabled
+    mutable size_t timed_resolved = 0;      // records [0, timed_resolved) hold their ms
+    hipEvent_t ring0[kTimingSlots] = {}, ring1[kTimingSlots] = {};
     ddp_comm_hook_fn hook = nullptr;
     void *hook_ctx = nullptr;
     // unused-parameter detection and no_sync [DDP-ch17 §17.33; PTD-notes §2.2.3, §2.2.4]
@@ -337,22 +396,28 @@ struct ddp_reducer {
         window_set = false;
     }
 
+    // builds the new group tables aside and swaps them in, so an allocation
+    // failure leaves the old grouping in place
     void set_groups(const int32_t *first, int32_t n)
     {
-        group_first.clear();
+        std::vector<int32_t> gf, go(size_t(pv.B)), gp;
         if (first)
-            group_first.assign(first, first + n);
+            gf.assign(first, first + n);
         else
-            for (int32_t b = 0; b < pv.B; ++b) group_first.push_back(b);
-        group_first.push_back(pv.B);
-        group_of.resize(pv.B);
-        for (size_t g = 0; g + 1 < group_first.size(); ++g)
-            for (int32_t b = group_first[g]; b < group_first[g + 1]; ++b) group_of[b] = int32_t(g);
+            for (int32_t b = 0; b < pv.B; ++b) gf.push_back(b);
+        gf.push_back(pv.B);
+        for (size_t g = 0; g + 1 < gf.size(); ++g)
+            for (int32_t b = gf[g]; b < gf[g + 1]; ++b) go[b] = int32_t(g);
+        gp.assign(gf.size() - 1, 0);
+        for (int b = 0; b < pv.B; ++b) gp[go[b]] += pending.empty() ? 0 : pending[b];
+        group_first.swap(gf);
+        group_of.swap(go);
+        group_pending.swap(gp);
     }
 
     void count_groups()
     {
-        group_pending.assign(group_first.size() - 1, 0);
+        std::fill(group_pending.begin(), group_pending.end(), 0);
         for (int b = 0; b < pv.B; ++b) group_pending[group_of[b]] += pending[b];
     }
 
@@ -381,26 +446,55 @@ struct ddp_reducer {
 
 namespace {
 
+// Copies the durations of timing records [r->timed_resolved, upto) from
+// their event pairs to the host records, waiting for those launches.
+int resolve_timings(const ddp_reducer *r, size_t upto)
+{
+    for (size_t i = r->timed_resolved; i < upto; ++i) {
+        const size_t slot = i % kTimingSlots;
+        hipError_t e = hipEventSynchronize(r->ring1[slot]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&r->timed[i].ms, r->ring0[slot], r->ring1[slot]);
+        if (e != hipSuccess) return hip_fail("reading a launch's timing events", e);
+        r->timed_resolved = i + 1;
+    }
+    return DDP_OK;
+}
+
 // Reduction of buckets [b0, b1) (consecutive, so their tiles are one
 // contiguous range of the tile table) as one kernel launch on stream s.
+// With timing on, the launch is bracketed by the next event pair of the
+// ring; a pair still holding an unread launch is read first (waiting for
+// that launch, kTimingSlots launches back).
 int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
 {
     if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device buffers");
     hipError_t e;
-    size_t slot = r->timed_bucket.size();
+    const size_t rec = r->timed.size();
+    const size_t slot = rec % kTimingSlots;
     if (r->timing) {
-        while (r->t0.size() <= slot) {
-            hipEvent_t a = nullptr, c = nullptr;
-            e = hipEventCreateWithFlags(&a, hipEventDisableSystemFence);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&c, hipEventDisableSystemFence);
+        if (rec >= kTimingSlots) {
+            const int rc = resolve_timings(r, rec - kTimingSlots + 1);
+            if (rc != DDP_OK) return rc;
+        }
+        if (!r->ring0[slot]) {
+            e = hipEventCreateWithFlags(&r->ring0[slot], hipEventDisableSystemFence);
             if (e != hipSuccess) {
-                if (a) (void)hipEventDestroy(a);
+                r->ring0[slot] = nullptr;
                 return hip_fail("hipEventCreate", e);
             }
-            r->t0.push_back(a);
-            r->t1.push_back(c);
         }
-        if ((e = hipEventRecord(r->t0[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
+        if (!r->ring1[slot]) {
+            e = hipEventCreateWithFlags(&r->ring1[slot], hipEventDisableSystemFence);
+            if (e != hipSuccess) {
+                r->ring1[slot] = nullptr;
+                return hip_fail("hipEventCreate", e);
+            }
+        }
+        r->timed.push_back({b0, b1 - b0, 0.0f});   // may throw: nothing is enqueued yet
+        if ((e = hipEventRecord(r->ring0[slot], s)) != hipSuccess) {
+            r->timed.pop_back();
+            return hip_fail("hipEventRecord", e);
+        }
     }
     const int32_t tile0 = r->pv.tile_begin[b0];
     const int32_t tiles = r->pv.tile_begin[b1 - 1] + r->pv.tile_count[b1 - 1] - tile0;
@@ -417,11 +511,13 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
         e = ddp::launch_mean(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
         break;
     }
-    if (e != hipSuccess) return hip_fail("bucket reduce launch", e);
-    if (r->timing) {
-        if ((e = hipEventRecord(r->t1[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
-        r->timed_bucket.push_back(b0);
-        r->timed_count.push_back(b1 - b0);
+    if (e != hipSuccess) {
+        if (r->timing) r->timed.pop_back();
+        return hip_fail("bucket reduce launch", e);
+    }
+    if (r->timing && (e = hipEventRecord(r->ring1[slot], s)) != hipSuccess) {
+        r->timed.pop_back();
+        return hip_fail("hipEventRecord", e);
     }
     return DDP_OK;
 }
@@ -499,11 +595,22 @@ int launch_buckets(ddp_reducer *r, int32_t b0, int32_t b1)
                                         " not launched: the launch of bucket " + std::to_string(r->failed_bucket) +
                                         " failed earlier in this backward");
     int32_t at = b0;
-    const int rc = issue_buckets(r, b0, b1, &at);
+    int rc;
+    try {   // next already moved past these buckets: a throw must still count as a failed launch
+        rc = issue_buckets(r, b0, b1, &at);
+    } catch (const std::bad_alloc &) {
+        rc = fail(DDP_ERR_NOMEM, kNoMemText);
+    } catch (...) {
+        rc = fail(DDP_ERR_INVALID, "internal error: unexpected exception while launching buckets");
+    }
     if (rc != DDP_OK) {
         r->failed_bucket = at;
         r->failed_code = rc;
-        r->failed_msg = g_err;
+        try {
+            r->failed_msg.assign(ddp_last_error());
+        } catch (...) {
+            r->failed_msg.clear();
+        }
     }
     return rc;
 }
@@ -533,14 +640,14 @@ int mark_one(ddp_reducer *r, int32_t param)
             if (r->masks[q] == 0 && q != param) mark_state(r, q);
     }
     if (r->ready[param])
-        return fail(DDP_ERR_ALREADY_READY,
-                    "gradient " + std::to_string(param) + " was marked ready twice in one backward pass");
+        return fail(DDP_ERR_ALREADY_READY, "Expected to mark a variable ready only once: gradient " +
+                                               std::to_string(param) + " was marked ready twice in this backward pass");
     mark_state(r, param);
     r->advance();
     return DDP_OK;
 }
 
-void destroy_events(ddp_reducer *r)
+void destroy_events(ddp_reducer *r) noexcept
 {
     for (auto &ev : r->stage_ev)
         if (ev) {
@@ -553,22 +660,36 @@ void destroy_events(ddp_reducer *r)
     if (r->ev_ready) (void)hipEventDestroy(r->ev_ready);
     if (r->ev_done) (void)hipEventDestroy(r->ev_done);
     if (r->ev_host) (void)hipEventDestroy(r->ev_host);
-    for (auto e : r->t0)
-        if (e) (void)hipEventDestroy(e);
-    for (auto e : r->t1)
-        if (e) (void)hipEventDestroy(e);
+    if (r->ev_tables) (void)hipEventDestroy(r->ev_tables);
+    if (r->ev_foreign) (void)hipEventDestroy(r->ev_foreign);
+    r->ev_tables = r->ev_foreign = nullptr;
+    for (int i = 0; i < kTimingSlots; ++i) {
+        if (r->ring0[i]) (void)hipEventDestroy(r->ring0[i]);
+        if (r->ring1[i]) (void)hipEventDestroy(r->ring1[i]);
+        r->ring0[i] = r->ring1[i] = nullptr;
+    }
     r->ev_ready = r->ev_done = r->ev_host = nullptr;
-    r->t0.clear();
-    r->t1.clear();
 }
+
+// Deleter of a reducer: its events and staging, then the object.
+struct ReducerRelease {
+    void operator()(ddp_reducer *r) const noexcept
+    {
+        if (!r) return;
+        destroy_events(r);
+        delete r;
+    }
+};
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char *ddp_last_error(void) { return g_err.c_str(); }
+// The entry points' bodies; the extern "C" definitions below run each one
+// through guarded().
 
-int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t *order, int32_t order_mode,
+
+int ddp_plan_buckets_impl(int32_t n_params, const int64_t *param_bytes, const int32_t *order, int32_t order_mode,
                      int64_t cap_bytes, int64_t first_cap_bytes, int32_t *bucket_of, int64_t *offset_in_bucket,
                      int32_t *bucket_params, int32_t *bucket_nparams, int64_t *bucket_bytes, int32_t *n_buckets)
 {
@@ -635,7 +756,7 @@ int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t
     return DDP_OK;
 }
 
-size_t ddp_workspace_bytes(const ddp_reducer_desc *desc)
+size_t ddp_workspace_bytes_impl(const ddp_reducer_desc *desc)
 {
     PlanView pv;
     if (validate(desc, pv) != DDP_OK) return 0;
@@ -643,15 +764,18 @@ size_t ddp_workspace_bytes(const ddp_reducer_desc *desc)
     return layout_of(pv).total;
 }
 
-int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
+int ddp_reducer_create_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
 {
     if (!out) return fail(DDP_ERR_INVALID, "out is NULL");
-    ddp_reducer *r = new (std::nothrow) ddp_reducer();
-    if (!r) return fail(DDP_ERR_INVALID, "out of host memory");
+    // released with its events and staging on every early return, and when
+    // an allocation throws
+    std::unique_ptr<ddp_reducer, ReducerRelease> r(new (std::nothrow) ddp_reducer());
+    if (!r) return fail(DDP_ERR_NOMEM, kNoMemText);
     int rc = validate(desc, r->pv);
-    if (rc != DDP_OK) {
-        delete r;
-        return rc;
+    if (rc != DDP_OK) return rc;
+    if (r->pv.find_unused) {   // sized once: later updates of the tables allocate nothing
+        r->window.assign(size_t(r->pv.W) * r->pv.P, 0);
+        r->masks.assign(r->pv.P, 0);
     }
     PlanView &pv = r->pv;
     r->scale.s = 1.0f / float(pv.W);
@@ -663,34 +787,21 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
     if (r->device) {
         const bool copy_src = pv.mode != DDP_IN_F32_VIEW;
         rc = build_segments(pv, copy_src || pv.find_unused);
-        if (rc != DDP_OK) {
-            delete r;
-            return rc;
-        }
+        if (rc != DDP_OK) return rc;
         for (int w = 0; w < pv.W; ++w)
-            if (!desc->flat[w]) {
-                delete r;
-                return fail(DDP_ERR_INVALID, "flat buffer of replica " + std::to_string(w) + " is NULL");
-            }
+            if (!desc->flat[w]) return fail(DDP_ERR_INVALID, "flat buffer of replica " + std::to_string(w) + " is NULL");
         if (copy_src) {
-            if (pv.P > 0 && !desc->grads) {
-                delete r;
-                return fail(DDP_ERR_INVALID, "gradient pointer table is NULL");
-            }
+            if (pv.P > 0 && !desc->grads) return fail(DDP_ERR_INVALID, "gradient pointer table is NULL");
             for (int w = 0; w < pv.W; ++w)
                 for (int32_t p = 0; p < pv.P; ++p)
-                    if (pv.numel[p] > 0 && !desc->grads[size_t(w) * pv.P + p]) {
-                        delete r;
+                    if (pv.numel[p] > 0 && !desc->grads[size_t(w) * pv.P + p])
                         return fail(DDP_ERR_INVALID, "gradient pointer is NULL");
-                    }
         }
         const Layout lay = layout_of(pv);
         if (!desc->workspace || desc->workspace_bytes < lay.total ||
-            reinterpret_cast<uintptr_t>(desc->workspace) % 16) {
-            delete r;
+            reinterpret_cast<uintptr_t>(desc->workspace) % 16)
             return fail(DDP_ERR_INVALID, "workspace missing, misaligned or smaller than " +
                                              std::to_string(lay.total) + " bytes");
-        }
         // Vector body of a segment: it starts at the first element whose
         // destination address is 256-byte aligned, so every wave's 1 KiB store
         // run covers whole cache lines (a store run that straddles lines costs
@@ -735,10 +846,7 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
             r->device_masks = r->masks;
         }
         hipError_t e = hipMemcpy(desc->workspace, host.data(), lay.total, hipMemcpyHostToDevice);
-        if (e != hipSuccess) {
-            delete r;
-            return hip_fail("workspace upload", e);
-        }
+        if (e != hipSuccess) return hip_fail("workspace upload", e);
         uint8_t *ws = static_cast<uint8_t *>(desc->workspace);
         r->tables.grads = copy_src ? reinterpret_cast<const void *const *>(ws + lay.grads_off) : nullptr;
         r->tables.flat = reinterpret_cast<float *const *>(ws + lay.flat_off);
@@ -761,21 +869,19 @@ int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
             e = hipHostMalloc(reinterpret_cast<void **>(&r->stage), 2 * sizeof(DeviceSeg) * pv.segs.size());
             for (int k = 0; k < 2 && e == hipSuccess; ++k)
                 e = hipEventCreateWithFlags(&r->stage_ev[k], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_tables, hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_foreign, hipEventDisableTiming);
         }
-        if (e != hipSuccess) {
-            destroy_events(r);
-            delete r;
-            return hip_fail("reducer setup (device attributes, events, staging)", e);
-        }
+        if (e != hipSuccess) return hip_fail("reducer setup (device attributes, events, staging)", e);
     }
-    if (pv.find_unused) r->window.assign(size_t(pv.W) * pv.P, 0);
+    r->ready_order.reserve(size_t(pv.P));   // a backward's marks then allocate nothing
     r->set_groups(nullptr, 0);
     r->reset();
-    *out = r;
+    *out = r.release();
     return DDP_OK;
 }
 
-int ddp_reducer_destroy(ddp_reducer *r)
+int ddp_reducer_destroy_impl(ddp_reducer *r)
 {
     if (!r) return DDP_OK;
     // reductions still queued on the comm stream read and write the caller's
@@ -785,25 +891,24 @@ int ddp_reducer_destroy(ddp_reducer *r)
         e = hipEventRecord(r->ev_host, r->comm);
         if (e == hipSuccess) e = hipEventSynchronize(r->ev_host);
     }
-    destroy_events(r);
-    delete r;
+    ReducerRelease()(r);
     return e == hipSuccess ? DDP_OK : hip_fail("waiting for outstanding reductions", e);
 }
 
-int ddp_prepare_for_backward(ddp_reducer *r)
+int ddp_prepare_for_backward_impl(ddp_reducer *r)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (r->in_iteration())
         return fail(DDP_ERR_UNFINISHED,
-                    "the previous iteration's reduction never finished before a new one was prepared; "
-                    "gradients never marked ready: " + list_params(r->unready()));
+                    "Expected to have finished reduction in the prior iteration before starting a new one. "
+                    "Parameter indices which did not receive grad: " + list_params(r->unready()));
     if (r->failed_bucket >= 0 && !r->finished) r->end_window();   // a failed backward never finished
     r->reset();
     r->sync = r->require_sync;
     return DDP_OK;
 }
 
-int ddp_mark_ready(ddp_reducer *r, int32_t param)
+int ddp_mark_ready_impl(ddp_reducer *r, int32_t param)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     const int32_t b0 = r->next;
@@ -812,7 +917,7 @@ int ddp_mark_ready(ddp_reducer *r, int32_t param)
     return launch_buckets(r, b0, r->next);
 }
 
-int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done)
+int ddp_mark_ready_many_impl(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done)
 {
     if (n_done) *n_done = 0;
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
@@ -825,25 +930,39 @@ int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_
     }
     // buckets completed by the marks that succeeded are launched even when a
     // later mark failed; the first error is the one reported
-    const std::string err = rc != DDP_OK ? g_err : std::string();
+    const std::string err = rc != DDP_OK ? std::string(ddp_last_error()) : std::string();
     const int lrc = launch_buckets(r, b0, r->next);
-    if (rc != DDP_OK) {
-        g_err = err;
-        return rc;
-    }
+    if (rc != DDP_OK) return fail(rc, err);
     return lrc;
 }
 
-int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream)
+int ddp_bucket_reduce_impl(ddp_reducer *r, int32_t bucket, void *stream)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (bucket < 0 || bucket >= r->pv.B) return fail(DDP_ERR_INVALID, "bucket index out of range");
     if (r->in_iteration() && bucket >= r->next)
         return fail(DDP_ERR_ORDER, "bucket " + std::to_string(bucket) + " still waits for gradients");
-    return enqueue_reduce(r, bucket, bucket + 1, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // With unused detection the segment table (it carries the replica masks)
+    // is rewritten on the comm stream once per synchronized backward. A
+    // reduction on another stream is ordered after the last rewrite, and the
+    // next rewrite after it.
+    const bool foreign = r->device && r->pv.find_unused && s != r->comm;
+    hipError_t e = hipSuccess;
+    if (foreign) {
+        e = hipEventRecord(r->ev_tables, r->comm);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, r->ev_tables, 0);
+        if (e != hipSuccess) return hip_fail("ordering a reduction after the mask upload", e);
+    }
+    const int rc = enqueue_reduce(r, bucket, bucket + 1, s);
+    if (rc != DDP_OK || !foreign) return rc;
+    e = hipEventRecord(r->ev_foreign, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(r->comm, r->ev_foreign, 0);
+    if (e != hipSuccess) return hip_fail("ordering the next mask upload after a reduction", e);
+    return DDP_OK;
 }
 
-int ddp_finish(ddp_reducer *r, int32_t host_blocking)
+int ddp_finish_impl(ddp_reducer *r, int32_t host_blocking)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (!r->sync) {           // no_sync: nothing was reduced, the used tables keep accumulating
@@ -872,8 +991,8 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
         }
     }
     if (r->next < r->pv.B)
-        return fail(DDP_ERR_NOT_READY,
-                    "buckets still wait for gradients never marked ready: " + list_params(r->unready()));
+        return fail(DDP_ERR_NOT_READY, "Backward ended with buckets never reduced. "
+                                       "Parameter indices which did not receive grad: " + list_params(r->unready()));
     if (r->device) {
         hipError_t e = hipSuccess;
         if (r->compute != r->comm) {
@@ -891,14 +1010,14 @@ int ddp_finish(ddp_reducer *r, int32_t host_blocking)
     return DDP_OK;
 }
 
-int ddp_set_require_sync(ddp_reducer *r, int32_t sync)
+int ddp_set_require_sync_impl(ddp_reducer *r, int32_t sync)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     r->require_sync = sync != 0;
     return DDP_OK;
 }
 
-int ddp_set_local_used(ddp_reducer *r, const uint8_t *used)
+int ddp_set_local_used_impl(ddp_reducer *r, const uint8_t *used)
 {
     if (!r || !used) return fail(DDP_ERR_INVALID, "NULL argument");
     if (!r->pv.find_unused) return fail(DDP_ERR_INVALID, "unused-parameter detection is off for this reducer");
@@ -913,7 +1032,7 @@ int ddp_set_local_used(ddp_reducer *r, const uint8_t *used)
     return DDP_OK;
 }
 
-int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
+int ddp_register_comm_hook_impl(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     r->hook = fn;
@@ -921,7 +1040,7 @@ int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
     return DDP_OK;
 }
 
-int ddp_set_bucket_groups(ddp_reducer *r, const int32_t *first_bucket, int32_t n_groups)
+int ddp_set_bucket_groups_impl(ddp_reducer *r, const int32_t *first_bucket, int32_t n_groups)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (r->in_iteration())
@@ -939,7 +1058,7 @@ int ddp_set_bucket_groups(ddp_reducer *r, const int32_t *first_bucket, int32_t n
     return DDP_OK;
 }
 
-int ddp_set_workgroups_per_cu(ddp_reducer *r, int32_t n)
+int ddp_set_workgroups_per_cu_impl(ddp_reducer *r, int32_t n)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (n > 8) return fail(DDP_ERR_INVALID, "workgroups per CU must be at most 8 (or 0: automatic, < 0: no cap)");
@@ -947,14 +1066,14 @@ int ddp_set_workgroups_per_cu(ddp_reducer *r, int32_t n)
     return DDP_OK;
 }
 
-int ddp_get_launch_lds(const ddp_reducer *r, int32_t *lds_bytes)
+int ddp_get_launch_lds_impl(const ddp_reducer *r, int32_t *lds_bytes)
 {
     if (!r || !lds_bytes) return fail(DDP_ERR_INVALID, "NULL argument");
     *lds_bytes = int32_t(r->launch_lds());
     return DDP_OK;
 }
 
-int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook)
+int ddp_register_builtin_hook_impl(ddp_reducer *r, int32_t hook)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (hook != DDP_HOOK_ALLREDUCE && hook != DDP_HOOK_BF16_COMPRESS && hook != DDP_HOOK_FP16_COMPRESS)
@@ -965,7 +1084,7 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook)
     return DDP_OK;
 }
 
-int ddp_get_bucket(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t *flat_offset_bytes,
+int ddp_get_bucket_impl(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t *flat_offset_bytes,
                    int32_t *n_params)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
@@ -976,7 +1095,7 @@ int ddp_get_bucket(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t
     return DDP_OK;
 }
 
-int ddp_get_bucket_params(const ddp_reducer *r, int32_t bucket, int32_t *params)
+int ddp_get_bucket_params_impl(const ddp_reducer *r, int32_t bucket, int32_t *params)
 {
     if (!r || !params) return fail(DDP_ERR_INVALID, "NULL argument");
     if (bucket < 0 || bucket >= r->pv.B) return fail(DDP_ERR_INVALID, "bucket index out of range");
@@ -984,7 +1103,7 @@ int ddp_get_bucket_params(const ddp_reducer *r, int32_t bucket, int32_t *params)
     return DDP_OK;
 }
 
-int ddp_get_ready_order(const ddp_reducer *r, int32_t *order, int32_t *n)
+int ddp_get_ready_order_impl(const ddp_reducer *r, int32_t *order, int32_t *n)
 {
     if (!r || !n) return fail(DDP_ERR_INVALID, "NULL argument");
     *n = int32_t(r->ready_order.size());
@@ -992,40 +1111,164 @@ int ddp_get_ready_order(const ddp_reducer *r, int32_t *order, int32_t *n)
     return DDP_OK;
 }
 
-int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched)
+int ddp_get_launched_impl(const ddp_reducer *r, int32_t *n_launched)
 {
     if (!r || !n_launched) return fail(DDP_ERR_INVALID, "NULL argument");
     *n_launched = r->next;
     return DDP_OK;
 }
 
-int ddp_set_timing(ddp_reducer *r, int32_t enable)
+int ddp_set_timing_impl(ddp_reducer *r, int32_t enable)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
     if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device");
     r->timing = enable != 0;
     if (r->timing) {
-        r->timed_bucket.clear();
-        r->timed_count.clear();
+        r->timed.clear();
+        r->timed_resolved = 0;
     }
     return DDP_OK;
 }
 
-int ddp_get_timings(const ddp_reducer *r, int32_t *first_bucket, int32_t *n_buckets, float *ms, int32_t capacity,
+int ddp_get_timings_impl(const ddp_reducer *r, int32_t *first_bucket, int32_t *n_buckets, float *ms, int32_t capacity,
                     int32_t *n)
 {
     if (!r || !n || capacity < 0) return fail(DDP_ERR_INVALID, "bad argument");
-    *n = int32_t(r->timed_bucket.size());
+    if (r->timed.size() > size_t(std::numeric_limits<int32_t>::max()))
+        return fail(DDP_ERR_INVALID, "more timing records than an int32 count holds");
+    *n = int32_t(r->timed.size());
     const int32_t m = std::min(capacity, *n);
+    if (ms && m > 0) {
+        const int rc = resolve_timings(r, size_t(m));
+        if (rc != DDP_OK) return rc;
+    }
     for (int32_t i = 0; i < m; ++i) {
-        if (first_bucket) first_bucket[i] = r->timed_bucket[i];
-        if (n_buckets) n_buckets[i] = r->timed_count[i];
-        if (ms) {
-            hipError_t e = hipEventElapsedTime(&ms[i], r->t0[i], r->t1[i]);
-            if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);
-        }
+        if (first_bucket) first_bucket[i] = r->timed[i].first;
+        if (n_buckets) n_buckets[i] = r->timed[i].count;
+        if (ms) ms[i] = r->timed[i].ms;
     }
     return DDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ddp_last_error(void) { return g_err_fixed ? g_err_fixed : g_err.c_str(); }
+
+int ddp_plan_buckets(int32_t n_params, const int64_t *param_bytes, const int32_t *order, int32_t order_mode, int64_t cap_bytes, int64_t first_cap_bytes, int32_t *bucket_of, int64_t *offset_in_bucket, int32_t *bucket_params, int32_t *bucket_nparams, int64_t *bucket_bytes, int32_t *n_buckets)
+{
+    return guarded([&] { return ddp_plan_buckets_impl(n_params, param_bytes, order, order_mode, cap_bytes, first_cap_bytes, bucket_of, offset_in_bucket, bucket_params, bucket_nparams, bucket_bytes, n_buckets); });
+}
+
+size_t ddp_workspace_bytes(const ddp_reducer_desc *desc)
+{
+    size_t n = 0;
+    guarded([&] {
+        n = ddp_workspace_bytes_impl(desc);
+        return DDP_OK;
+    });
+    return n;
+}
+
+int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
+{
+    return guarded([&] { return ddp_reducer_create_impl(desc, out); });
+}
+
+int ddp_reducer_destroy(ddp_reducer *r)
+{
+    return guarded([&] { return ddp_reducer_destroy_impl(r); });
+}
+
+int ddp_prepare_for_backward(ddp_reducer *r)
+{
+    return guarded([&] { return ddp_prepare_for_backward_impl(r); });
+}
+
+int ddp_mark_ready(ddp_reducer *r, int32_t param)
+{
+    return guarded([&] { return ddp_mark_ready_impl(r, param); });
+}
+
+int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_t *n_done)
+{
+    return guarded([&] { return ddp_mark_ready_many_impl(r, params, n, n_done); });
+}
+
+int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream)
+{
+    return guarded([&] { return ddp_bucket_reduce_impl(r, bucket, stream); });
+}
+
+int ddp_finish(ddp_reducer *r, int32_t host_blocking)
+{
+    return guarded([&] { return ddp_finish_impl(r, host_blocking); });
+}
+
+int ddp_set_require_sync(ddp_reducer *r, int32_t sync)
+{
+    return guarded([&] { return ddp_set_require_sync_impl(r, sync); });
+}
+
+int ddp_set_local_used(ddp_reducer *r, const uint8_t *used)
+{
+    return guarded([&] { return ddp_set_local_used_impl(r, used); });
+}
+
+int ddp_register_comm_hook(ddp_reducer *r, ddp_comm_hook_fn fn, void *ctx)
+{
+    return guarded([&] { return ddp_register_comm_hook_impl(r, fn, ctx); });
+}
+
+int ddp_set_bucket_groups(ddp_reducer *r, const int32_t *first_bucket, int32_t n_groups)
+{
+    return guarded([&] { return ddp_set_bucket_groups_impl(r, first_bucket, n_groups); });
+}
+
+int ddp_set_workgroups_per_cu(ddp_reducer *r, int32_t n)
+{
+    return guarded([&] { return ddp_set_workgroups_per_cu_impl(r, n); });
+}
+
+int ddp_get_launch_lds(const ddp_reducer *r, int32_t *lds_bytes)
+{
+    return guarded([&] { return ddp_get_launch_lds_impl(r, lds_bytes); });
+}
+
+int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook)
+{
+    return guarded([&] { return ddp_register_builtin_hook_impl(r, hook); });
+}
+
+int ddp_get_bucket(const ddp_reducer *r, int32_t bucket, int64_t *bytes, int64_t *flat_offset_bytes, int32_t *n_params)
+{
+    return guarded([&] { return ddp_get_bucket_impl(r, bucket, bytes, flat_offset_bytes, n_params); });
+}
+
+int ddp_get_bucket_params(const ddp_reducer *r, int32_t bucket, int32_t *params)
+{
+    return guarded([&] { return ddp_get_bucket_params_impl(r, bucket, params); });
+}
+
+int ddp_get_ready_order(const ddp_reducer *r, int32_t *order, int32_t *n)
+{
+    return guarded([&] { return ddp_get_ready_order_impl(r, order, n); });
+}
+
+int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched)
+{
+    return guarded([&] { return ddp_get_launched_impl(r, n_launched); });
+}
+
+int ddp_set_timing(ddp_reducer *r, int32_t enable)
+{
+    return guarded([&] { return ddp_set_timing_impl(r, enable); });
+}
+
+int ddp_get_timings(const ddp_reducer *r, int32_t *first_bucket, int32_t *n_buckets, float *ms, int32_t capacity, int32_t *n)
+{
+    return guarded([&] { return ddp_get_timings_impl(r, first_bucket, n_buckets, ms, capacity, n); });
 }
 
 }  // extern "C"

@@ -2,7 +2,10 @@
  *
  * C ABI of libddp.so. Plain pointers and sizes only; every function returns
  * an int status (DDP_OK = 0, negative on error, text in ddp_last_error())
- * unless stated otherwise, and never throws.
+ * unless stated otherwise. No exception ever leaves an entry point: host
+ * memory exhaustion anywhere in a call is DDP_ERR_NOMEM, and a call that
+ * fails that way leaves the reducer as it was before the call (a launch
+ * that could not be issued counts as a failed launch, see ddp_mark_ready).
  *
  * Sources (cited by tag and section):
  *   [DDP-ch17]    "PyTorch 训练框架内核深度解析", chapter 17
@@ -51,13 +54,19 @@ extern "C" {
 enum {
     DDP_OK = 0,
     DDP_ERR_INVALID = -1,        /* bad argument or inconsistent plan                                */
-    DDP_ERR_ALREADY_READY = -2,  /* a gradient marked ready twice in one backward [DDP-ch17 §17.16]  */
+    DDP_ERR_ALREADY_READY = -2,  /* a gradient marked ready twice in one backward [DDP-ch17 §17.16];
+                                    text "Expected to mark a variable ready only once: ..."        */
     DDP_ERR_UNFINISHED = -3,     /* new iteration while buckets of the last one never launched
-                                    [DDP-ch17 §17.6; L15 §4.2]                                      */
-    DDP_ERR_NOT_READY = -4,      /* finish while some buckets still wait for gradients             */
+                                    [DDP-ch17 §17.6; L15 §4.2]; text "Expected to have finished
+                                    reduction in the prior iteration before starting a new one.
+                                    Parameter indices which did not receive grad: i j ..."         */
+    DDP_ERR_NOT_READY = -4,      /* finish while some buckets still wait for gradients; the text
+                                    ends "Parameter indices which did not receive grad: i j ..."
+                                    [DDP-ch17 §17.6]                                                */
     DDP_ERR_ORDER = -5,          /* explicit reduce of a bucket whose gradients are not all ready   */
     DDP_ERR_HIP = -6,            /* a HIP runtime call failed (its text is in ddp_last_error)        */
-    DDP_ERR_HOOK = -7            /* a registered communication hook returned non-zero               */
+    DDP_ERR_HOOK = -7,           /* a registered communication hook returned non-zero               */
+    DDP_ERR_NOMEM = -8           /* host memory ran out (an allocation inside the library failed)  */
 };
 
 enum {
@@ -156,20 +165,27 @@ typedef struct {
 } ddp_reducer_desc;
 
 /* Device workspace the reducer needs for its tables (segments, tiles,
- * pointers). Returns 0 and sets ddp_last_error() if the desc is invalid. */
+ * pointers): the device-side counterpart of the Reducer's bucket list
+ * [DDP-ch17 §17.2]. Returns 0 and sets ddp_last_error() if the desc is
+ * invalid (or host memory runs out). */
 size_t ddp_workspace_bytes(const ddp_reducer_desc *desc);
 
-/* Validates the desc, copies the plan, builds and uploads the device tables
- * (synchronously) and leaves the reducer ready for its first backward.
- * *out is set only on success. */
+/* The Reducer [DDP-ch17 §17.2, §17.14]: built once from the parameter list
+ * and its bucket plan, it holds the buckets, each bucket's pending count and
+ * the per-gradient ready hooks' state. Validates the desc, copies the plan,
+ * builds and uploads the device tables (synchronously) and leaves the
+ * reducer ready for its first backward. *out is set only on success.
+ * Errors: DDP_ERR_INVALID (bad desc or buffers), DDP_ERR_HIP, DDP_ERR_NOMEM;
+ * nothing is left allocated on failure. */
 int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out);
 
-/* Waits for every reduction the reducer queued on its comm stream, then
- * releases host state, events and staging; the caller's buffers are
- * untouched and may be freed once this returns. Reductions the caller queued
- * on other streams through ddp_bucket_reduce are the caller's to wait for.
- * NULL is a no-op. The reducer is released even when the wait reports an
- * error (DDP_ERR_HIP). */
+/* Ends a Reducer [DDP-ch17 §17.2]: waits for every reduction it queued on
+ * its comm stream (as the end of backward waits for each bucket's
+ * collective, [DDP-ch17 §17.41]), then releases host state, events and
+ * staging; the caller's buffers are untouched and may be freed once this
+ * returns. Reductions the caller queued on other streams through
+ * ddp_bucket_reduce are the caller's to wait for. NULL is a no-op. The
+ * reducer is released even when the wait reports an error (DDP_ERR_HIP). */
 int ddp_reducer_destroy(ddp_reducer *r);
 
 /* Resets every bucket's pending count and the per-iteration ready set before
@@ -226,7 +242,11 @@ int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_
  * hook's arithmetic; a compression hook (ddp_register_builtin_hook) changes
  * the term and every add as described there. With unused-parameter
  * detection the reduction applies the replica masks last uploaded (all
- * replicas before the first synchronized backward's first launch). */
+ * replicas before the first synchronized backward's first launch); the
+ * masks travel in the segment table, which the comm stream rewrites, so on
+ * any other stream the reduction is made to wait for the work queued so far
+ * on the comm stream, and the comm stream to wait for the reduction (two
+ * events; results do not depend on the stream). */
 int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
 
 /* End of backward [DDP-ch17 §17.41; MegatronDDP §5]: checks that every bucket
@@ -342,21 +362,26 @@ int ddp_get_launched(const ddp_reducer *r, int32_t *n_launched);
 
 /* Per-launch timing: while enabled, each default reduction launch (one
  * bucket, or a coalesced group) is bracketed by two HIP events on the stream
- * it runs on (timing-only events, without the system-scope fence). Enabling
- * (again) starts a new record list; the events are kept and reused. The
- * list, and the event pool with it, grows by one record (two events) per
- * launch for as long as timing stays enabled; the pool is freed by
- * ddp_reducer_destroy.
+ * it runs on (timing-only events, without the system-scope fence). The
+ * events form a fixed ring of 256 pairs, created on first use and freed by
+ * ddp_reducer_destroy: when launch i reuses the pair of launch i - 256, the
+ * host first waits for that launch to complete and copies its duration into
+ * a host record (12 bytes per launch). Enabling (again) starts a new record
+ * list.
  * ddp_get_timings copies up to `capacity` records (launch order) of the
  * launches since timing was last enabled: the first bucket, the number of
- * buckets the launch covered, and the kernel's duration in ms. The caller
- * must first wait for those launches to complete (e.g. ddp_finish with
- * host_blocking). *n = number of records. Any output array may be NULL. */
+ * buckets the launch covered, and the kernel's duration in ms. With ms
+ * non-NULL it waits for the launches it reports to complete. *n = number of
+ * records. Any output array may be NULL. */
 int ddp_set_timing(ddp_reducer *r, int32_t enable);
 int ddp_get_timings(const ddp_reducer *r, int32_t *first_bucket, int32_t *n_buckets, float *ms, int32_t capacity,
                     int32_t *n);
 
-/* Text of the last error on this thread ("" if none). Never NULL. */
+/* Text of the last error on this thread ("" if none). Never NULL. Where the
+ * pages give PyTorch's wording of a Reducer error, the text starts with it
+ * (DDP_ERR_ALREADY_READY, DDP_ERR_UNFINISHED, DDP_ERR_NOT_READY above:
+ * [DDP-ch17 §17.6, §17.16; L15 §4.2]). The pointer stays valid until the
+ * next failing call on the same thread. */
 const char *ddp_last_error(void);
 
 #ifdef __cplusplus

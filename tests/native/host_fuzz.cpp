@@ -9,17 +9,27 @@
 //    ddp_finish reports the failure;
 //  * a successful ddp_finish of a synchronized backward saw every bucket;
 //  * every status is one of the documented codes.
-// usage: host_fuzz SEEDS     exit status 0 when every sequence holds.
+// With "oom", one call in ten runs with operator new failing after a few
+// allocations: such a call may also return DDP_ERR_NOMEM, and every
+// invariant above must still hold (a launch that could not be issued counts
+// as a failed one).
+// usage: host_fuzz SEEDS [oom]     exit status 0 when every sequence holds.
 #include "ddp.h"
 
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <new>
 #include <random>
+#include <string>
 #include <vector>
 
+#include "failing_new.h"
+
 namespace {
+
+bool g_oom = false;
 
 struct Recorder {
     std::vector<int32_t> seen;   // buckets handed to the callback in this backward
@@ -48,7 +58,8 @@ void expect(bool ok, const char *what, int seed, int step)
 bool known_status(int rc)
 {
     return rc == DDP_OK || rc == DDP_ERR_INVALID || rc == DDP_ERR_ALREADY_READY || rc == DDP_ERR_UNFINISHED ||
-           rc == DDP_ERR_NOT_READY || rc == DDP_ERR_ORDER || rc == DDP_ERR_HIP || rc == DDP_ERR_HOOK;
+           rc == DDP_ERR_NOT_READY || rc == DDP_ERR_ORDER || rc == DDP_ERR_HIP || rc == DDP_ERR_HOOK ||
+           (g_oom && rc == DDP_ERR_NOMEM);
 }
 
 void run(int seed)
@@ -91,14 +102,20 @@ void run(int seed)
     expect(rc == DDP_OK && r, "create", seed, -1);
     if (rc != DDP_OK) return;
     Recorder rec;
+    rec.seen.reserve(size_t(B));   // the callback allocates nothing while allocations may fail
     ddp_register_comm_hook(r, on_bucket, &rec);
 
     bool sync = true, sync_next = true, prepared = false;
     std::vector<uint8_t> used(size_t(W) * P, 1);
     for (int step = 0; step < 200; ++step) {
         const int op = pick(0, 99);
+        // the budget applies to the library call of this step only; the
+        // checks after it allocate freely
+        const long budget = g_oom && pick(0, 9) == 0 ? pick(0, 4) : -1;
         if (op < 10) {                                    // prepare
+            g_new_budget = budget;
             rc = ddp_prepare_for_backward(r);
+            g_new_budget = -1;
             expect(known_status(rc), "prepare status", seed, step);
             if (rc == DDP_OK) {
                 rec.seen.clear();
@@ -108,22 +125,33 @@ void run(int seed)
                 prepared = true;
             }
         } else if (op < 60) {                             // one mark, sometimes out of range or repeated
-            rc = ddp_mark_ready(r, pick(-1, P));
+            const int p = pick(-1, P);
+            g_new_budget = budget;
+            rc = ddp_mark_ready(r, p);
+            g_new_budget = -1;
             expect(known_status(rc), "mark status", seed, step);
         } else if (op < 75) {                             // a batch of marks
             std::vector<int32_t> batch(pick(0, 6));
             for (auto &x : batch) x = pick(0, P - 1);
             int32_t done = -1;
+            g_new_budget = budget;
             rc = ddp_mark_ready_many(r, batch.data(), int32_t(batch.size()), &done);
+            g_new_budget = -1;
             expect(known_status(rc) && done >= 0 && done <= int32_t(batch.size()), "mark_many status", seed, step);
         } else if (op < 85) {                             // finish
             const size_t before = rec.seen.size();
+            g_new_budget = budget;
             rc = ddp_finish(r, 0);
+            g_new_budget = -1;
             expect(known_status(rc), "finish status", seed, step);
             if (rc == DDP_OK && prepared && sync) {
                 int32_t launched = -1;
                 ddp_get_launched(r, &launched);
                 expect(launched == B, "finish succeeded with buckets unlaunched", seed, step);
+                // every bucket reached the callback: none was lost to a launch
+                // that failed (a hook error, or an allocation failure)
+                expect(rec.seen.size() == size_t(B), "finish succeeded with a bucket never handed to the hook",
+                       seed, step);
             }
             if (rec.failed) expect(rc != DDP_OK || !sync, "finish hid a failed launch", seed, step);
             (void)before;
@@ -132,14 +160,18 @@ void run(int seed)
             ddp_set_require_sync(r, sync_next ? 1 : 0);
         } else if (op < 93) {                             // used tables
             for (auto &u : used) u = uint8_t(pick(0, 3) != 0);
+            g_new_budget = budget;
             rc = ddp_set_local_used(r, used.data());
+            g_new_budget = -1;
             expect(known_status(rc), "used status", seed, step);
         } else if (op < 97) {                             // regroup
             std::vector<int32_t> firsts;
             for (int b = 0; b < B; ++b)
                 if (b == 0 || pick(0, 2) == 0) firsts.push_back(b);
             if (pick(0, 5) == 0 && !firsts.empty()) firsts.back() = B + 3;   // invalid list
+            g_new_budget = budget;
             rc = ddp_set_bucket_groups(r, firsts.data(), int32_t(firsts.size()));
+            g_new_budget = -1;
             expect(known_status(rc), "groups status", seed, step);
         } else {                                          // introspection
             int64_t nb = 0, off = 0;
@@ -168,6 +200,7 @@ void run(int seed)
 int main(int argc, char **argv)
 {
     const int seeds = argc > 1 ? std::atoi(argv[1]) : 200;
+    g_oom = argc > 2 && std::string(argv[2]) == "oom";
     for (int s = 0; s < seeds; ++s) run(s);
     if (g_bad) {
         std::fprintf(stderr, "%d violations\n", g_bad);

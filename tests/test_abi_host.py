@@ -640,3 +640,46 @@ def test_random_api_sequences_match_the_oracle_model(seed):
         assert log[before:] == want, (seed, step, op, log[before:], want)
         assert ddp.ddp_get_launched(r) == model.next_bucket, (seed, step, op)
     ddp.ddp_reducer_destroy(r)
+
+
+def test_reducer_dropped_without_destroy_is_released_by_its_finalizer():
+    """A Reducer the caller drops without ddp_reducer_destroy is destroyed by
+    a finalizer (which keeps the objects the native reducer reads, such as
+    its workspace, referenced until then); an explicit destroy detaches the
+    finalizer, and a second destroy is a no-op."""
+    import gc
+    r, plan, log = host_reducer([4, 4, 4], 16, 16)
+    holder, fin = r._holder, r._finalizer
+    assert holder[0] and fin.alive
+    del r
+    gc.collect()
+    assert holder[0] is None and not fin.alive
+    r2, _, _ = host_reducer([4], 16, 16)
+    f2 = r2._finalizer
+    ddp.ddp_reducer_destroy(r2)
+    assert not f2.alive and r2.handle is None
+    ddp.ddp_reducer_destroy(r2)
+
+
+def test_error_texts_start_with_pytorchs_wording():
+    """The three Reducer errors the pages quote keep PyTorch's wording at the
+    start of the message [DDP-ch17 §17.6, §17.16], and list the gradients
+    that did not receive one, ascending."""
+    r, plan, log = host_reducer([4, 4, 4, 4], 16, 16)
+    ddp.ddp_mark_ready(r, 3)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_mark_ready(r, 3)
+    assert e.value.msg.startswith("Expected to mark a variable ready only once")
+    ddp.ddp_mark_ready(r, 0)
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_finish(r)
+    assert e.value.code == ddp.DDP_ERR_NOT_READY
+    assert e.value.msg.endswith("Parameter indices which did not receive grad: 1 2")
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.ddp_prepare_for_backward(r)
+    assert e.value.code == ddp.DDP_ERR_UNFINISHED
+    assert e.value.msg.startswith("Expected to have finished reduction in the prior iteration before "
+                                  "starting a new one.")
+    assert e.value.msg.endswith("Parameter indices which did not receive grad: 1 2")
+    ddp.ddp_reducer_destroy(r)
+
