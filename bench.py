@@ -426,8 +426,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="resnet50",
-                    help="tiny | resnet50 | bert_large | megatron_llama1b | sweep_w{W}_cap{MiB}")
+    # default: the largest workload that fits one GPU (Llama-style 1B, W = 16,
+    # bf16 wgrads accumulated into the fp32 main_grad, 152.5 GB per step)
+    ap.add_argument("--workload", default="megatron_llama1b",
+                    help="megatron_llama1b | resnet50 | bert_large | tiny | sweep_w{W}_cap{MiB}")
     ap.add_argument("--collective", default="all_reduce", choices=["all_reduce", "reduce_scatter"])
     ap.add_argument("--hook", default="none", choices=list(HOOKS),
                     help="built-in communication hook: the fp32 mean, or bf16 / fp16 compression")

@@ -327,3 +327,78 @@ def test_bert_large_sampled_with_unused_masks_and_bf16_hook():
     wl = wls.bert_large()
     say("case bert_large unused + bf16 hook sampled")
     _sampled_with_unused(wl, _seeded_used(wl.world, len(wl.numel), 13), hook=1)
+
+
+@pytest.mark.parametrize("W,mode,collective", [(4, 0, 0), (8, 2, 0), (16, 0, 1)])
+def test_hook_on_a_third_stream_with_changing_masks(W, mode, collective):
+    """A Python callback hook reduces every bucket on a third stream while
+    the used tables change from one backward to the next. The masks travel
+    in the segment table that the comm stream rewrites once per backward, so
+    the library orders each reduction on another stream after that upload,
+    and the next upload after the reduction. The test makes both orders
+    matter: in even backwards the comm stream is held busy before the
+    backward (so its upload lands after the third stream could have started
+    reducing), in odd ones the third stream waits before the first reduction
+    (so its reductions would still be pending when the next backward's
+    upload is queued). Each backward's results are snapshotted on the third stream and
+    all compared, bit for bit, with the oracle's fold under that backward's
+    used table."""
+    import synth
+    from expect import expected_flat, host_threads, oracle_plan, param_flat_ranges
+    torch = _torch()
+    wl = _small_workload(9700 + W + mode, W, mode)
+    P = len(wl.numel)
+    say(f"case third-stream hook {wl.name} P={P} collective={collective}")
+    run = URun(wl, collective)
+    ddp = run.ddp
+    third = torch.cuda.Stream()
+    first_bucket = [True]
+    third_wait_us = [0.0]
+
+    def hook(b):
+        if first_bucket[0]:
+            synth.spin_dev(third_wait_us[0], third.cuda_stream)   # the backward's reductions start late
+            first_bucket[0] = False
+        ddp.ddp_bucket_reduce(run.r, b, third.cuda_stream)
+        return 0
+
+    ddp.ddp_register_comm_hook(run.r, hook)
+    rng = random.Random(W * 7 + mode)
+    inputs0 = [run.flat_host(w) for w in range(W)]   # view/bf16 modes reduce in place: restore each time
+    tables, snaps = [], []
+    for it in range(4):
+        used = random_used(rng, W, P, p_unused=0.3, p_global=0.15)
+        tables.append(used)
+        if mode != 0:   # after the last snapshot, on the comm stream
+            run.comm.wait_stream(third)
+            with torch.cuda.stream(run.comm):
+                for w in range(W):
+                    run.inputs.flat[w][:run.total].copy_(torch.from_numpy(inputs0[w]), non_blocking=False)
+        if it % 2 == 0:
+            synth.spin_dev(6000.0, run.comm.cuda_stream)   # the mask upload lands late
+        third_wait_us[0] = 500.0 if it % 2 == 0 else 10000.0
+        first_bucket[0] = True
+        ddp.ddp_prepare_for_backward(run.r)
+        ddp.ddp_set_local_used(run.r, used)
+        gone = {p for p in range(P) if not any(used[w][p] for w in range(W))}
+        for p in range(P - 1, -1, -1):
+            if p not in gone:
+                ddp.ddp_mark_ready(run.r, p)
+        with torch.cuda.stream(third):
+            snaps.append([run.inputs.flat[w][:run.total].clone() for w in range(W)])
+        ddp.ddp_finish(run.r, host_blocking=False)
+    torch.cuda.synchronize()
+    oplan = oracle_plan(wl)
+    ranges = param_flat_ranges(wl, oplan)
+    for it, (used, snap) in enumerate(zip(tables, snaps)):
+        want = expected_flat(wl, oplan, wl.seed, nthreads=host_threads(), used=used)
+        untouched = np.zeros(run.total, dtype=bool)
+        for p, (lo, hi) in enumerate(ranges):
+            if not any(used[w][p] for w in range(W)):
+                untouched[lo:hi] = True
+        for w in range(W):
+            got = snap[w].cpu().numpy()
+            owned = owned_mask(run, w) if collective else np.ones(run.total, dtype=bool)
+            m = owned & ~untouched
+            assert_bits(got[m], want[m], f"{wl.name} backward {it} replica {w}")
+    run.close()
