@@ -51,8 +51,8 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 # one object per source; the kernel families compile in parallel
-SOURCES = ["reducer.cpp", "bucket_reduce.hip", "bucket_bf16_hook.hip", "bucket_fp16_hook.hip"]
-HEADERS = ["internal.h", "reduce_kernels.h"]
+SOURCES = ["reducer.cpp", "bucket_reduce.hip", "bucket_bf16_hook.hip", "bucket_fp16_hook.hip", "static_tables.hip"]
+HEADERS = ["internal.h", "reduce_kernels.h", "static_area.h"]
 
 
 BUILD_DIR = os.path.join(HERE, "_build")
@@ -140,6 +140,7 @@ def lib():
         sig = {
             "ddp_plan_buckets": [I32, P, P, I32, I64, I64, P, P, P, P, P, P],
             "ddp_reducer_create": [ctypes.POINTER(ddp_reducer_desc), ctypes.POINTER(ctypes.c_void_p)],
+            "ddp_reducer_create_static": [ctypes.POINTER(ddp_reducer_desc), ctypes.POINTER(ctypes.c_void_p)],
             "ddp_reducer_destroy": [P],
             "ddp_prepare_for_backward": [P],
             "ddp_mark_ready": [P, I32],
@@ -318,6 +319,17 @@ class Reducer:
 def ddp_reducer_create(desc: Desc) -> Reducer:
     h = ctypes.c_void_p()
     _check(lib().ddp_reducer_create(ctypes.byref(desc.c), ctypes.byref(h)))
+    return Reducer(h.value, desc)
+
+
+DDP_STATIC_TABLE_BYTES = 16 << 20
+
+
+def ddp_reducer_create_static(desc: Desc) -> Reducer:
+    """ddp_reducer_create with the device tables in the library's static
+    table area (no workspace, no device allocation)."""
+    h = ctypes.c_void_p()
+    _check(lib().ddp_reducer_create_static(ctypes.byref(desc.c), ctypes.byref(h)))
     return Reducer(h.value, desc)
 
 

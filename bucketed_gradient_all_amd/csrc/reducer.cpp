@@ -4,6 +4,7 @@
 // Sources are cited by tag and section; the tags are defined in include/ddp.h.
 #include "../../include/ddp.h"
 #include "internal.h"
+#include "static_area.h"
 
 #include <hip/hip_runtime_api.h>
 
@@ -299,6 +300,10 @@ struct ddp_reducer {
         return unsigned(std::min(bytes, lds_per_block));
     }
     KernelTables tables{};
+    // tables in the static area of this device (ddp_reducer_create_static),
+    // valid while the area's generation is the one this reducer claimed
+    int static_device = -1;
+    uint64_t static_generation = 0;
     hipStream_t compute = nullptr, comm = nullptr;
     // ev_ready: compute -> comm before a launch; ev_done: comm -> compute at
     // finish (device-scope release suffices between two streams of one
@@ -468,6 +473,10 @@ int resolve_timings(const ddp_reducer *r, size_t upto)
 int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
 {
     if (!r->device) return fail(DDP_ERR_INVALID, "reducer has no device buffers");
+    if (r->static_generation && ddp::static_table_generation(r->static_device) != r->static_generation)
+        return fail(DDP_ERR_INVALID, "this reducer's tables in the static table area of device " +
+                                         std::to_string(r->static_device) +
+                                         " were replaced by a later ddp_reducer_create_static");
     hipError_t e;
     const size_t rec = r->timed.size();
     const size_t slot = rec % kTimingSlots;
@@ -764,7 +773,9 @@ size_t ddp_workspace_bytes_impl(const ddp_reducer_desc *desc)
     return layout_of(pv).total;
 }
 
-int ddp_reducer_create_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
+// Creation shared by ddp_reducer_create (tables in the caller's workspace)
+// and ddp_reducer_create_static (tables in the library's static area).
+int create_reducer(const ddp_reducer_desc *desc, ddp_reducer **out, bool static_area)
 {
     if (!out) return fail(DDP_ERR_INVALID, "out is NULL");
     // released with its events and staging on every early return, and when
@@ -798,8 +809,25 @@ int ddp_reducer_create_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
                         return fail(DDP_ERR_INVALID, "gradient pointer is NULL");
         }
         const Layout lay = layout_of(pv);
-        if (!desc->workspace || desc->workspace_bytes < lay.total ||
-            reinterpret_cast<uintptr_t>(desc->workspace) % 16)
+        void *workspace = desc->workspace;
+        size_t workspace_bytes = desc->workspace_bytes;
+        if (static_area) {
+            // Unused detection stages its masks through pinned host memory,
+            // which this variant does not allocate.
+            if (pv.find_unused)
+                return fail(DDP_ERR_INVALID, "ddp_reducer_create_static does not support unused-parameter "
+                                             "detection (its mask staging would allocate pinned memory)");
+            int dev = -1;
+            hipError_t e = hipGetDevice(&dev);
+            if (e == hipSuccess) e = ddp::static_table_area(dev, &workspace, &workspace_bytes);
+            if (e != hipSuccess) return hip_fail("static table area", e);
+            if (lay.total > workspace_bytes)
+                return fail(DDP_ERR_INVALID, "the reducer's tables need " + std::to_string(lay.total) +
+                                                 " bytes; the static table area holds " +
+                                                 std::to_string(workspace_bytes) + " (DDP_STATIC_TABLE_BYTES)");
+            r->static_device = dev;
+        }
+        if (!workspace || workspace_bytes < lay.total || reinterpret_cast<uintptr_t>(workspace) % 16)
             return fail(DDP_ERR_INVALID, "workspace missing, misaligned or smaller than " +
                                              std::to_string(lay.total) + " bytes");
         // Vector body of a segment: it starts at the first element whose
@@ -845,9 +873,19 @@ int ddp_reducer_create_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
             r->segment_records(reinterpret_cast<DeviceSeg *>(host.data() + lay.segs_off));
             r->device_masks = r->masks;
         }
-        hipError_t e = hipMemcpy(desc->workspace, host.data(), lay.total, hipMemcpyHostToDevice);
+        // a static reducer claims the area before writing it: any earlier
+        // static reducer on this device refuses to launch from here on
+        hipError_t e = hipSuccess;
+        if (static_area) {
+            // reductions already queued by an earlier static reducer may still
+            // read the area: let the device drain before it is rewritten
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail("waiting for the device before rewriting the static table area", e);
+            r->static_generation = ddp::claim_static_table_area(r->static_device);
+        }
+        e = hipMemcpy(workspace, host.data(), lay.total, hipMemcpyHostToDevice);
         if (e != hipSuccess) return hip_fail("workspace upload", e);
-        uint8_t *ws = static_cast<uint8_t *>(desc->workspace);
+        uint8_t *ws = static_cast<uint8_t *>(workspace);
         r->tables.grads = copy_src ? reinterpret_cast<const void *const *>(ws + lay.grads_off) : nullptr;
         r->tables.flat = reinterpret_cast<float *const *>(ws + lay.flat_off);
         r->segs_dev = reinterpret_cast<DeviceSeg *>(ws + lay.segs_off);
@@ -879,6 +917,16 @@ int ddp_reducer_create_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
     r->reset();
     *out = r.release();
     return DDP_OK;
+}
+
+int ddp_reducer_create_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
+{
+    return create_reducer(desc, out, false);
+}
+
+int ddp_reducer_create_static_impl(const ddp_reducer_desc *desc, ddp_reducer **out)
+{
+    return create_reducer(desc, out, true);
 }
 
 int ddp_reducer_destroy_impl(ddp_reducer *r)
@@ -1174,6 +1222,11 @@ size_t ddp_workspace_bytes(const ddp_reducer_desc *desc)
 int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out)
 {
     return guarded([&] { return ddp_reducer_create_impl(desc, out); });
+}
+
+int ddp_reducer_create_static(const ddp_reducer_desc *desc, ddp_reducer **out)
+{
+    return guarded([&] { return ddp_reducer_create_static_impl(desc, out); });
 }
 
 int ddp_reducer_destroy(ddp_reducer *r)

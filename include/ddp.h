@@ -179,6 +179,29 @@ size_t ddp_workspace_bytes(const ddp_reducer_desc *desc);
  * nothing is left allocated on failure. */
 int ddp_reducer_create(const ddp_reducer_desc *desc, ddp_reducer **out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * reducer as ddp_reducer_create, with its device tables in a static table
+ * area the library owns instead of a caller-allocated workspace
+ * (desc->workspace and desc->workspace_bytes are ignored). The call and the
+ * reducer allocate no device memory: the area is a device array of
+ * DDP_STATIC_TABLE_BYTES per GPU, which every GPU the library runs on holds
+ * until the process ends. The caller still passes the gradient and flat
+ * buffers and both streams.
+ *  - One area per device, shared by every static reducer on it: creating a
+ *    static reducer first waits for the device to drain (so reductions
+ *    already queued by an earlier one finish), then rewrites the area; the
+ *    earlier static reducer then refuses to launch (DDP_ERR_INVALID). Calls
+ *    that overlap on one device (from several host threads) race.
+ *  - Unused-parameter detection (desc->find_unused) is not supported: its
+ *    mask staging needs pinned host memory (DDP_ERR_INVALID).
+ *  - Tables larger than DDP_STATIC_TABLE_BYTES are refused (DDP_ERR_INVALID,
+ *    with the size needed); ddp_workspace_bytes gives that size.
+ * It also creates the reducer's HIP events and host-side state, as
+ * ddp_reducer_create does. Released by ddp_reducer_destroy. */
+#define DDP_STATIC_TABLE_BYTES (16u << 20)
+int ddp_reducer_create_static(const ddp_reducer_desc *desc, ddp_reducer **out);
+
 /* Ends a Reducer [DDP-ch17 §17.2]: waits for every reduction it queued on
  * its comm stream (as the end of backward waits for each bucket's
  * collective, [DDP-ch17 §17.41]), then releases host state, events and

@@ -332,6 +332,43 @@ void check_out_of_memory()
     fake::g_logging = true;
 }
 
+// ddp_reducer_create_static: the tables go to the static area (the
+// workspace is ignored), the device drains before the area is rewritten, a
+// later static reducer makes the earlier one refuse to launch, and unused
+// detection and oversized tables are refused.
+void check_static_area()
+{
+    fake::g_logging = true;
+    Model a(4, 20, 8000, false, 31), b(2, 5, 1000, false, 32);
+    a.d.workspace = nullptr;   // ignored by the static variant
+    a.d.workspace_bytes = 0;
+    b.d.workspace = nullptr;
+    b.d.workspace_bytes = 0;
+    ddp_reducer *ra = nullptr, *rb = nullptr;
+    fake::reset_log();
+    expect(ddp_reducer_create_static(&a.d, &ra) == DDP_OK && ra, "static: create");
+    bool drained = false;
+    for (const auto &c : fake::g_log) drained |= !std::strcmp(c.what, "device_sync");
+    expect(drained, "static: the device was not drained before the area was written");
+    expect(backward(ra, a) == DDP_OK, "static: backward");
+    expect(ddp_reducer_create_static(&b.d, &rb) == DDP_OK && rb, "static: second create");
+    expect(backward(rb, b) == DDP_OK, "static: second reducer's backward");
+    int rc = backward(ra, a);
+    expect(rc == DDP_ERR_INVALID && std::strstr(ddp_last_error(), "replaced"),
+           "static: the first reducer launched from a replaced table area");
+    expect(ddp_bucket_reduce(ra, 0, kComm) == DDP_ERR_INVALID, "static: explicit reduce from a replaced area");
+    // a regular reducer is unaffected by the static area
+    ddp_reducer *rr = nullptr;
+    Model c(3, 7, 4000, false, 33);
+    expect(ddp_reducer_create(&c.d, &rr) == DDP_OK && backward(rr, c) == DDP_OK, "static: regular reducer");
+    // unused detection is refused
+    Model u(2, 5, 1000, true, 34);
+    ddp_reducer *ru = nullptr;
+    expect(ddp_reducer_create_static(&u.d, &ru) == DDP_ERR_INVALID && !ru, "static: unused detection accepted");
+    expect(ddp_reducer_destroy(ra) == DDP_OK && ddp_reducer_destroy(rb) == DDP_OK && ddp_reducer_destroy(rr) == DDP_OK,
+           "static: destroy");
+}
+
 }  // namespace
 
 int main()
@@ -339,6 +376,7 @@ int main()
     check_timing_ring();
     check_foreign_stream_masks();
     check_out_of_memory();
+    check_static_area();
     if (g_bad) {
         std::fprintf(stderr, "%d violations\n", g_bad);
         return 1;

@@ -9,9 +9,12 @@
 // elapsed time between two events is the start event's stamp (so a test can
 // tell which launch a duration was read from). Work completes at once:
 // queries and waits succeed. Every call is appended to a log the test reads.
+// The static table area is host memory here.
 #include "fake_hip.h"
 
+#include "ddp.h"
 #include "internal.h"
+#include "static_area.h"
 
 #include <cstdlib>
 #include <cstring>
@@ -177,9 +180,41 @@ const char *hipGetErrorString(hipError_t)
     return "fake HIP error";
 }
 
+hipError_t hipDeviceSynchronize(void)
+{
+    Call c{};
+    c.what = "device_sync";
+    fake::log_call(c);
+    return hipSuccess;
+}
+
 }  // extern "C"
 
 namespace ddp {
+
+// The static table area, as host memory: one area, device 0 only.
+namespace {
+alignas(256) unsigned char g_area[DDP_STATIC_TABLE_BYTES];
+uint64_t g_area_generation = 0;
+}  // namespace
+
+hipError_t static_table_area(int device, void **ptr, size_t *bytes)
+{
+    if (device != 0) return hipErrorInvalidDevice;
+    *ptr = g_area;
+    *bytes = sizeof(g_area);
+    return hipSuccess;
+}
+
+uint64_t claim_static_table_area(int)
+{
+    return ++g_area_generation;
+}
+
+uint64_t static_table_generation(int)
+{
+    return g_area_generation;
+}
 
 hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles, unsigned,
                        hipStream_t s)

@@ -15,6 +15,7 @@ CSRC = os.path.join(ROOT, "bucketed_gradient_all_amd", "csrc")
 
 STUB = r'''
 #include "internal.h"
+#include "static_area.h"
 namespace ddp {
 hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned, hipStream_t)
 { return hipErrorInvalidValue; }
@@ -24,6 +25,9 @@ hipError_t launch_bf16_hook(int, int, bool, const Scale &, const KernelTables &,
 hipError_t launch_fp16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned,
                             hipStream_t)
 { return hipErrorInvalidValue; }
+hipError_t static_table_area(int, void **, size_t *) { return hipErrorNoDevice; }
+uint64_t claim_static_table_area(int) { return 0; }
+uint64_t static_table_generation(int) { return 0; }
 }
 '''
 
