@@ -447,6 +447,8 @@ def main():
                          "(default: synth.device.REPLICA_STAGGER)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain-layout", action="store_true",
+                    help="skip the extra kernel timing with the replicas' buffers laid out without a stagger")
     ap.add_argument("--backward-ms", type=float, default=20.0,
                     help="synthetic backward for the overlap measurement (0 disables it)")
     ap.add_argument("--overlap-steps", type=int, default=5)
@@ -520,6 +522,8 @@ def main():
     ddp.ddp_register_builtin_hook(s.r, hook)
     ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
     bytes_per_step = sum(bucket_alg_of(s, wl))
+    launch_lds = ddp.ddp_get_launch_lds(s.r)
+    stagger = s.stagger
 
     for _ in range(args.warmup):
         s.step()
@@ -578,20 +582,33 @@ def main():
                          "kernel_GBps_all": round(sum(bucket_alg) * args.steps / (float(pms.sum()) / 1e3) / 1e9, 1)
                          if pms.size else None}
 
-    overlap = None
-    if args.backward_ms > 0:
+    def overlap_of(kind):
+        """The step with a synthetic backward of backward_ms on the compute
+        stream (one piece per bucket, each followed by that bucket's ready
+        call), against the serial order and the backward alone."""
         us = args.backward_ms * 1e3
+        s.backward_kind = kind
         s.step(backward_us=us)
         t_ov = s.timed(args.overlap_steps, backward_us=us) / args.overlap_steps
         t_se = s.timed(args.overlap_steps, backward_us=us, serial=True) / args.overlap_steps
         s.timed(1, backward_us=us, backward_only=True)
         t_bw = s.timed(args.overlap_steps, backward_us=us, backward_only=True) / args.overlap_steps
-        overlap = {"backward_ms": args.backward_ms, "backward_kind": args.backward_kind,
-                   "backward_alone_ms": round(t_bw * 1e3, 3),
-                   "step_ms_overlapped": round(t_ov * 1e3, 3),
-                   "step_ms_serial": round(t_se * 1e3, 3),
-                   "exposed_ms": round((t_ov - t_bw) * 1e3, 3),
-                   "reduce_ms_alone": round(step_s * 1e3, 3)}
+        s.backward_kind = args.backward_kind
+        return {"backward_ms": args.backward_ms, "backward_kind": kind,
+                "backward_alone_ms": round(t_bw * 1e3, 3),
+                "step_ms_overlapped": round(t_ov * 1e3, 3),
+                "step_ms_serial": round(t_se * 1e3, 3),
+                "exposed_ms": round((t_ov - t_bw) * 1e3, 3),
+                "overlap_gain_ms": round((t_se - t_ov) * 1e3, 3),
+                "reduce_ms_alone": round(step_s * 1e3, 3)}
+
+    overlap = overlap_gemm = None
+    if args.backward_ms > 0:
+        # a backward that takes no resources (a one-workgroup wait), and one
+        # of bf16 GEMMs that compete with the reduction for CUs, LDS and HBM
+        overlap = overlap_of(args.backward_kind)
+        if args.backward_kind != "gemm":
+            overlap_gemm = overlap_of("gemm")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -600,6 +617,30 @@ def main():
         s.step()
         torch.cuda.synchronize()
         cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds, hook, used)
+
+    # The same launches with the replicas' buffers laid out plainly (no
+    # stagger: replica w's buffers at the start of their allocations), in a
+    # second set of buffers: the rate a caller gets without the placement
+    # the harness uses (see synth.device.REPLICA_STAGGER).
+    plain = None
+    if not args.no_plain_layout and s.stagger != 0:
+        streams = (s.compute, s.comm)
+        s.close()
+        ps = Session(wl, arena=args.arena, stagger=0, backward_kind=args.backward_kind, used=used, streams=streams)
+        ddp.ddp_register_builtin_hook(ps.r, hook)
+        ddp.ddp_set_workgroups_per_cu(ps.r, args.workgroups_per_cu)
+        for _ in range(max(args.warmup, 3)):
+            ps.step()
+        torch.cuda.synchronize()
+        ddp.ddp_set_timing(ps.r, True)
+        ps.timed(args.steps)
+        pfirst, pcount, pms = ddp.ddp_get_timings(ps.r)
+        ddp.ddp_set_timing(ps.r, False)
+        pbytes = sum(sum(bucket_alg[f:f + c]) for f, c in zip(pfirst, pcount))
+        prate = pbytes / (float(pms.sum()) / 1e3) / 1e9 if pms.size else 0.0
+        plain = {"replica_stagger_bytes": 0, "achieved": round(prate, 1), "frac": round(prate / HBM_PEAK_GBPS, 4),
+                 "launches": int(pms.size)}
+        ps.close()
 
     # the committed counters describe the default launch and layout only
     default_setup = args.workgroups_per_cu == 0 and args.stagger is None and not args.arena
@@ -627,8 +668,8 @@ def main():
                        "unused_pairs": int((used == 0).sum()),
                        "gradients_unused_everywhere": int((~used.any(axis=0)).sum())},
                    "workgroups_per_cu": args.workgroups_per_cu,
-                   "replica_stagger_bytes": s.stagger,
-                   "launch_lds_bytes": ddp.ddp_get_launch_lds(s.r),
+                   "replica_stagger_bytes": stagger,
+                   "launch_lds_bytes": launch_lds,
                    "parallelism": "1 GPU, W replicas in HBM"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "bus_bw_GBps": round(bus, 2),
@@ -645,10 +686,13 @@ def main():
                                                 if scrubbed is not None else None)},
         "per_bucket_launch": per_bucket_launch,
         "overlap": overlap,
+        "overlap_gemm_backward": overlap_gemm,
+        "plain_layout": plain,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    s.close()
+    if s.r is not None:
+        s.close()
 
 
 if __name__ == "__main__":

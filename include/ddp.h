@@ -363,12 +363,19 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
  *          for the reduce-scatter and for the all-reduce at W = 5..32;
  *          except that the all-reduce at W = 3, 4 runs one per CU (none in
  *          DDP_IN_BF16_ACCUM_F32 mode) and the DDP_IN_BF16_ACCUM_F32
- *          all-reduce at W = 16 runs one per CU;
+ *          all-reduce at W = 16 runs one per CU. A launch issued while the
+ *          caller's backward still has work queued on the compute stream
+ *          [PTD-notes §2.2.3] runs at most one per CU, which leaves more of
+ *          each CU to the backward's kernels (work queued there counts as the
+ *          caller's once the wait that the last ddp_finish left on the
+ *          compute stream is done; before that, as with back-to-back
+ *          reductions, the launch keeps the rule above);
  *   n < 0  no cap (no LDS reserved; occupancy limited by registers only);
  *   1..8   at most n per CU.
  * Takes effect at the next launch; results do not depend on it.
  * Errors: DDP_ERR_INVALID for n > 8. ddp_get_launch_lds reports the LDS bytes
- * each workgroup of the next launch will reserve (0: none). */
+ * each workgroup of the next launch will reserve when no backward runs beside
+ * it (0: none). */
 int ddp_set_workgroups_per_cu(ddp_reducer *r, int32_t n);
 int ddp_get_launch_lds(const ddp_reducer *r, int32_t *lds_bytes);
 

@@ -369,10 +369,44 @@ void check_static_area()
            "static: destroy");
 }
 
+// The occupancy rule of a launch: the tuned cap (two workgroups per CU at
+// W = 8) for back-to-back reductions and the exposed tail, one per CU beside
+// a running backward. A backward is taken to be running when the compute
+// stream has work queued and the wait that the last finish left there is
+// done (or there was no finish yet).
+void check_launch_occupancy()
+{
+    fake::g_logging = true;
+    Model m(8, 12, 1 << 30, false, 41);   // one bucket: one launch per backward
+    ddp_reducer *r = nullptr;
+    expect(ddp_reducer_create(&m.d, &r) == DDP_OK, "occupancy: create");
+    int32_t tuned = 0;
+    expect(ddp_get_launch_lds(r, &tuned) == DDP_OK && tuned == 56832, "occupancy: two per CU at W = 8");
+    auto launch_lds = [&]() -> long {
+        fake::reset_log();
+        if (backward(r, m) != DDP_OK) return -1;
+        for (const auto &c : fake::g_log)
+            if (!std::strcmp(c.what, "launch")) return long(c.lds);
+        return -2;
+    };
+    fake::g_stream_query = hipErrorNotReady;   // the caller's backward is queued; no finish yet
+    expect(launch_lds() == 83968, "occupancy: first backward beside queued work: one per CU");
+    fake::g_event_query = hipErrorNotReady;    // compute still waits for the last reduction
+    expect(launch_lds() == tuned, "occupancy: back-to-back reductions keep the tuned cap");
+    fake::g_event_query = hipSuccess;          // that wait is done: the queued work is a backward
+    expect(launch_lds() == 83968, "occupancy: beside a running backward: one per CU");
+    fake::g_stream_query = hipSuccess;         // compute drained: the exposed tail
+    expect(launch_lds() == tuned, "occupancy: drained compute stream keeps the tuned cap");
+    fake::g_stream_query = hipErrorNotReady;
+    expect(ddp_set_workgroups_per_cu(r, 2) == DDP_OK && launch_lds() == tuned, "occupancy: explicit cap kept");
+    expect(ddp_reducer_destroy(r) == DDP_OK, "occupancy: destroy");
+}
+
 }  // namespace
 
 int main()
 {
+    check_launch_occupancy();
     check_timing_ring();
     check_foreign_stream_masks();
     check_out_of_memory();

@@ -26,6 +26,7 @@ long g_live_events = 0;
 long g_max_live_events = 0;
 long g_stamp = 0;
 hipError_t g_stream_query = hipErrorNotReady;
+hipError_t g_event_query = hipSuccess;
 bool g_logging = true;
 
 namespace {
@@ -39,13 +40,14 @@ void log_call(Call c)
     if (g_logging) g_log.push_back(c);
 }
 
-hipError_t launch(const char *what, hipStream_t s, int32_t tile0, int32_t tiles)
+hipError_t launch(const char *what, hipStream_t s, int32_t tile0, int32_t tiles, unsigned lds)
 {
     Call c{};
     c.what = what;
     c.stream = s;
     c.a = tile0;
     c.b = tiles;
+    c.lds = lds;
     log_call(c);
     return hipSuccess;
 }
@@ -115,6 +117,12 @@ hipError_t hipStreamQuery(hipStream_t)
     return fake::g_stream_query;
 }
 
+hipError_t hipEventQuery(hipEvent_t event)
+{
+    if (!event) return hipErrorInvalidHandle;
+    return fake::stamp_of(event) < 0 ? hipSuccess : fake::g_event_query;
+}
+
 hipError_t hipEventSynchronize(hipEvent_t event)
 {
     if (!event) return hipErrorInvalidHandle;
@@ -171,7 +179,8 @@ hipError_t hipGetDevice(int *device)
 
 hipError_t hipDeviceGetAttribute(int *value, hipDeviceAttribute_t attr, int)
 {
-    *value = attr == hipDeviceAttributeMaxSharedMemoryPerMultiprocessor ? 160 * 1024 : 64 * 1024;
+    (void)attr;   // gfx950: 160 KiB of LDS per CU, all of it available to one workgroup
+    *value = 160 * 1024;
     return hipSuccess;
 }
 
@@ -216,22 +225,22 @@ uint64_t static_table_generation(int)
     return g_area_generation;
 }
 
-hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles, unsigned,
-                       hipStream_t s)
+hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles,
+                       unsigned lds, hipStream_t s)
 {
-    return fake::launch("launch", s, tile0, tiles);
+    return fake::launch("launch", s, tile0, tiles, lds);
 }
 
 hipError_t launch_bf16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles,
-                            unsigned, hipStream_t s)
+                            unsigned lds, hipStream_t s)
 {
-    return fake::launch("launch", s, tile0, tiles);
+    return fake::launch("launch", s, tile0, tiles, lds);
 }
 
 hipError_t launch_fp16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles,
-                            unsigned, hipStream_t s)
+                            unsigned lds, hipStream_t s)
 {
-    return fake::launch("launch", s, tile0, tiles);
+    return fake::launch("launch", s, tile0, tiles, lds);
 }
 
 }  // namespace ddp
