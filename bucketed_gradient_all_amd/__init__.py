@@ -276,14 +276,15 @@ def ddp_workspace_bytes(desc: Desc) -> int:
     return int(n)
 
 
-def _release(holder: list, keep) -> None:
+def _release(holder: list, keep, L) -> None:
     """Finalizer of a Reducer dropped without ddp_reducer_destroy: destroys
     the native reducer (which waits for its comm stream) while `keep` (the
     workspace and host tables it reads) is still referenced, so nothing the
-    queued reductions use goes back to an allocator first."""
+    queued reductions use goes back to an allocator first. L is the library
+    that created the reducer: only its destroy knows the reducer's layout."""
     h, holder[0] = holder[0], None
     if h:
-        lib().ddp_reducer_destroy(h)
+        L.ddp_reducer_destroy(h)
 
 
 class Reducer:
@@ -295,7 +296,8 @@ class Reducer:
         self._hook = None
         self._hook_error: Optional[BaseException] = None
         self.workspace = None
-        self._finalizer = weakref.finalize(self, _release, self._holder, [desc])
+        self._lib = lib()   # the library that created the reducer destroys it
+        self._finalizer = weakref.finalize(self, _release, self._holder, [desc], self._lib)
 
     @property
     def handle(self):
@@ -305,7 +307,7 @@ class Reducer:
         """Keeps obj (e.g. the device workspace) referenced until the native
         reducer is destroyed, explicitly or by the finalizer."""
         self._finalizer.detach()
-        self._finalizer = weakref.finalize(self, _release, self._holder, [self.desc, obj])
+        self._finalizer = weakref.finalize(self, _release, self._holder, [self.desc, obj], self._lib)
 
     def check(self, rc: int) -> int:
         """_check for calls that may run the Python hook: an exception the
@@ -338,7 +340,7 @@ def ddp_reducer_destroy(r: Reducer) -> None:
     if h:
         r._holder[0] = None
         r._finalizer.detach()
-        _check(lib().ddp_reducer_destroy(h))
+        _check(r._lib.ddp_reducer_destroy(h))
 
 
 def ddp_prepare_for_backward(r: Reducer) -> None:
