@@ -435,13 +435,26 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
 // scalar registers; a table read after a store would have to go through the
 // vector memory path and wait for every outstanding store.
 //
-// The 32-slot instances run at most two workgroups per CU under the automatic
-// cap (two waves per SIMD). Saying so lets the compiler keep all 32 loads of a
-// group in flight before the first add; aiming at four waves per SIMD, it
-// holds back the later loads until earlier ones return (measured: +4% for
+// Waves per SIMD an instance is compiled for: the most the automatic cap
+// lets share a SIMD. The 32-slot instances run at most two workgroups per CU
+// (two waves per SIMD); saying so lets the compiler keep all 32 loads of a
+// group in flight before the first add, where aiming at more waves it holds
+// back the later loads until earlier ones return (measured: +4% for
 // reduce-scatter and +2% with unused masks at W = 32, no change at W = 16).
+// The all-reduce of bf16 wgrads into fp32 main_grad at 16 replicas runs one
+// workgroup per CU (one wave per SIMD), so its 64 loads per thread may use
+// the whole register file (measured in one process on one set of buffers:
+// 5691-5694 against 5605-5651 GB/s on the Megatron Llama-1B workload).
+template <int W, int MODE, bool RS, bool PARTIAL>
+constexpr int max_waves_per_simd()
+{
+    if (W == 16 && MODE == MODE_BF16 && !RS && !PARTIAL) return 1;
+    return W >= 32 ? 2 : 8;
+}
+
 template <int W, int MODE, int HOOK, bool RS, bool USED, bool PARTIAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, W >= 32 ? 2 : 8))) void reduce_fixed(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, max_waves_per_simd<W, MODE, RS, PARTIAL>())))
+void reduce_fixed(
     KernelTables T, int32_t tile_begin, Scale sc, int n)
 {
     constexpr int NOUT = RS ? 1 : W;

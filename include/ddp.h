@@ -372,6 +372,9 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
  *          reductions, the launch keeps the rule above);
  *   n < 0  no cap (no LDS reserved; occupancy limited by registers only);
  *   1..8   at most n per CU.
+ * The instance for the DDP_IN_BF16_ACCUM_F32 all-reduce at W = 16 is compiled
+ * for one wave per SIMD (all of its loads in flight), so it holds one
+ * workgroup per CU whatever n allows.
  * Takes effect at the next launch; results do not depend on it.
  * Errors: DDP_ERR_INVALID for n > 8. ddp_get_launch_lds reports the LDS bytes
  * each workgroup of the next launch will reserve when no backward runs beside
