@@ -351,6 +351,63 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0, used=None):
     }
 
 
+def run_stream_probe(args):
+    """HBM rate of W equal-offset streams at the reduction's launch shape (one
+    4 KiB tile of every buffer per 256-thread workgroup): W reads, W writes,
+    or a copy of W buffers to W others, for W = 1 ... 32, at one and two
+    workgroups per CU and uncapped. These kernels move data and compute
+    nothing: they measure what the access pattern itself reaches on this GPU,
+    the ceiling the reduction's fold and stores sit under. One JSON line per W."""
+    import torch
+    import synth
+    from synth.device import REPLICA_STAGGER
+    stagger = REPLICA_STAGGER if args.stagger is None else args.stagger
+    if stagger < 0 or stagger % 256:
+        raise SystemExit("--stream-probe needs a stagger that is a multiple of 256 bytes")
+    total = args.stream_probe_mib << 20
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def buffers(n, nbytes):
+        # buffer k starts k * stagger bytes into its allocation, as the
+        # harness places replicas
+        held = [torch.full(((nbytes + n * stagger) // 4,), 0.5, dtype=torch.float32, device="cuda")
+                for _ in range(n)]
+        ptrs = [h.data_ptr() + k * stagger for k, h in enumerate(held)]
+        return held, torch.tensor(ptrs, dtype=torch.int64, device="cuda")
+
+    def rate(kind, W, src, dst, tiles, k, nbytes, reps=10):
+        run = lambda: synth.stream_probe_dev(kind, W, src, dst, sink.data_ptr(), tiles, k, st.cuda_stream)
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) / reps) / 1e6, 1)
+
+    for W in (1, 2, 4, 8, 16, 32):
+        row = {"stream_probe": True, "W": W, "stagger": stagger, "bytes_per_pass": total,
+               "read_GBps": {}, "write_GBps": {}, "copy_GBps": {}}
+        size = total // W // 4096 * 4096
+        held, tab = buffers(W, size)
+        for k in (1, 2, 0):
+            row["read_GBps"][str(k)] = rate(synth.PROBE_READ, W, tab.data_ptr(), 0, size // 4096, k, W * size)
+            row["write_GBps"][str(k)] = rate(synth.PROBE_WRITE, W, 0, tab.data_ptr(), size // 4096, k, W * size)
+        del held, tab
+        size = total // (2 * W) // 4096 * 4096
+        hs, ts = buffers(W, size)
+        hd, td = buffers(W, size)
+        for k in (1, 2, 0):
+            row["copy_GBps"][str(k)] = rate(synth.PROBE_COPY, W, ts.data_ptr(), td.data_ptr(), size // 4096, k,
+                                            2 * W * size)
+        del hs, ts, hd, td
+        torch.cuda.empty_cache()
+        print(json.dumps(row), flush=True)
+
+
 def run_sweep(args):
     """Bucket-size sweep (60M fp32 parameters as 6000 tensors of 10K): for
     every W and cap, the reduction alone (one launch per bucket and
@@ -462,6 +519,9 @@ def main():
     ap.add_argument("--sweep-out", default="")
     ap.add_argument("--sweep-group-mib", type=int, default=0,
                     help="also measure bucket groups of at least this many MiB (0: off)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only measure the HBM rate of W equal-offset read / write / copy streams and exit")
+    ap.add_argument("--stream-probe-mib", type=int, default=8192, help="bytes moved per probe pass (MiB)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this size (for HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -498,6 +558,10 @@ def main():
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / reps
         print(json.dumps({"copy_bytes": nbytes, "read_plus_write_GBps": round(2 * nbytes / dt / 1e9, 1)}))
+        return
+
+    if args.stream_probe:
+        run_stream_probe(args)
         return
 
     if args.sweep:

@@ -88,6 +88,9 @@ def dev_lib():
                                      ctypes.c_int32, ctypes.c_void_p]
         L.synth_copy_dev.restype = ctypes.c_int
         L.synth_copy_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.synth_stream_probe_dev.restype = ctypes.c_int
+        L.synth_stream_probe_dev.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
         L.synth_spin_dev.restype = ctypes.c_int
         L.synth_spin_dev.argtypes = [ctypes.c_double, ctypes.c_void_p]
         L.synth_last_error.restype = ctypes.c_char_p
@@ -154,6 +157,19 @@ def fill_dev(entries: Sequence[tuple], dist: int, scale: float, bf16: bool = Fal
 
 def copy_dev(dst: int, src: int, nbytes: int, stream: int = 0) -> None:
     rc = dev_lib().synth_copy_dev(dst, src, nbytes, stream)
+    if rc != 0:
+        raise RuntimeError(dev_lib().synth_last_error().decode())
+
+
+PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
+
+
+def stream_probe_dev(kind: int, world: int, src_table: int, dst_table: int, sink: int, tiles: int,
+                     workgroups_per_cu: int, stream: int = 0) -> None:
+    """Enqueues one HBM-rate probe over `world` equal-offset buffers (see
+    synth.h): read (PROBE_READ), write (PROBE_WRITE) or copy (PROBE_COPY)."""
+    rc = dev_lib().synth_stream_probe_dev(kind, world, src_table, dst_table, sink, tiles, workgroups_per_cu,
+                                          stream)
     if rc != 0:
         raise RuntimeError(dev_lib().synth_last_error().decode())
 

@@ -72,6 +72,17 @@ int synth_fill_dev(const synth_entry *entries, int32_t n_entries, int dist, floa
 /* Plain 16-byte vector copy of `bytes` (a multiple of 16) between 16-byte
  * aligned device buffers; a known-size kernel for calibrating HBM counters. */
 int synth_copy_dev(void *dst, const void *src, int64_t bytes, void *stream);
+/* HBM-rate probe over `world` (1, 2, 4, 8, 16 or 32) equal-sized buffers whose
+ * device pointers sit in the device tables src_table / dst_table: `tiles`
+ * workgroups of 256 threads, each moving one 4 KiB tile of every buffer
+ * (every buffer holds tiles * 4096 bytes, 16-byte aligned). kind 0 reads the
+ * sources (sink: a device array of 256 uint32 that is written only if a
+ * loaded word pattern is all ones), 1 writes the destinations, 2 copies
+ * source k to destination k. workgroups_per_cu (0..8; 0 = no cap) bounds the
+ * workgroups resident per CU the way the reduction does, with reserved LDS.
+ * Enqueued on `stream`; returns -1 on bad arguments or a launch error. */
+int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const void *dst_table, void *sink,
+                           int64_t tiles, int32_t workgroups_per_cu, void *stream);
 /* One workgroup that waits `microseconds` of wall-clock time on the device
  * (at most 10 s); a stand-in for a slice of backward compute. */
 int synth_spin_dev(double microseconds, void *stream);

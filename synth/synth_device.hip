@@ -1,7 +1,8 @@
 // Device half of the synthetic gradient generator (definition in synth.h),
-// plus two workload stand-ins used around the reduction: a plain vector copy
-// of known size (to calibrate HBM byte counters) and a wall-clock wait that
-// stands in for a slice of backward compute.
+// plus workload stand-ins used around the reduction: a plain vector copy of
+// known size (to calibrate HBM byte counters), a wall-clock wait that stands
+// in for a slice of backward compute, and probes of the HBM rate of W
+// equal-offset streams (data movement only).
 #include "synth.h"
 
 #include <hip/hip_runtime.h>
@@ -89,6 +90,54 @@ __global__ __launch_bounds__(256) void copy_kernel(float4 *__restrict__ dst, con
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// One 4 KiB tile of every one of W buffers per 256-thread workgroup, the
+// reduction's launch shape. KIND 0 reads the W sources (the loaded words are
+// OR-ed and compared with a pattern the probe's fill never produces, so the
+// loads stay live; nothing is stored), KIND 1 writes a constant to the W
+// destinations, KIND 2 copies source k to destination k. Nontemporal loads
+// and stores, as in the reduction.
+typedef float probe_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned probe_u4 __attribute__((ext_vector_type(4)));
+
+template <int W, int KIND>
+__global__ __launch_bounds__(256) void stream_probe_kernel(const probe_f4 *const *__restrict__ src,
+                                                           probe_f4 *const *__restrict__ dst,
+                                                           unsigned *__restrict__ sink)
+{
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (KIND == 1) {
+        const probe_f4 c = {1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+        for (int k = 0; k < W; ++k) __builtin_nontemporal_store(c, dst[k] + i);
+        return;
+    }
+    probe_f4 v[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) v[k] = __builtin_nontemporal_load(src[k] + i);
+    if (KIND == 2) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) __builtin_nontemporal_store(v[k], dst[k] + i);
+        return;
+    }
+    probe_u4 bits = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < W; ++k) bits |= __builtin_bit_cast(probe_u4, v[k]);
+    if ((bits.x & bits.y & bits.z & bits.w) == 0xFFFFFFFFu) sink[threadIdx.x] = bits.x;
+}
+
+template <int W>
+hipError_t launch_probe(int kind, const void *src, const void *dst, void *sink, unsigned grid, unsigned lds,
+                        hipStream_t st)
+{
+    const auto *s = static_cast<const probe_f4 *const *>(src);
+    auto *d = static_cast<probe_f4 *const *>(const_cast<void *>(dst));
+    auto *k = static_cast<unsigned *>(sink);
+    if (kind == 0) hipLaunchKernelGGL((stream_probe_kernel<W, 0>), dim3(grid), dim3(256), lds, st, s, d, k);
+    else if (kind == 1) hipLaunchKernelGGL((stream_probe_kernel<W, 1>), dim3(grid), dim3(256), lds, st, s, d, k);
+    else hipLaunchKernelGGL((stream_probe_kernel<W, 2>), dim3(grid), dim3(256), lds, st, s, d, k);
+    return hipGetLastError();
+}
+
 __global__ void spin_kernel(uint64_t ticks, uint64_t max_iter)
 {
     uint64_t t0 = wall_clock64();
@@ -173,6 +222,46 @@ int synth_copy_dev(void *dst, const void *src, int64_t bytes, void *stream)
                        static_cast<float4 *>(dst), static_cast<const float4 *>(src), n16);
     hipError_t err = hipGetLastError();
     return err == hipSuccess ? 0 : fail("copy launch", err);
+}
+
+int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const void *dst_table, void *sink,
+                           int64_t tiles, int32_t workgroups_per_cu, void *stream)
+{
+    if (kind < 0 || kind > 2 || tiles < 0 || tiles > int64_t(0x7FFFFFFF) || workgroups_per_cu < 0 ||
+        workgroups_per_cu > 8 || (kind != 1 && (!src_table || !sink)) || (kind != 0 && !dst_table)) {
+        g_err = "synth_stream_probe_dev: bad kind, tile count, cap or table";
+        return -1;
+    }
+    if (tiles == 0) return 0;
+    // the occupancy cap as the reduction sets it: LDS reserved so that at
+    // most workgroups_per_cu workgroups fit on a CU (0: no cap)
+    unsigned lds = 0;
+    if (workgroups_per_cu > 0) {
+        int dev = 0, per_cu = 0, per_block = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err == hipSuccess)
+            err = hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+        if (err == hipSuccess) err = hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (err != hipSuccess) return fail("LDS sizes", err);
+        int bytes = per_cu / (workgroups_per_cu + 1) + 2048;
+        bytes = (bytes + 255) / 256 * 256;
+        lds = unsigned(std::min(bytes, per_block));
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const unsigned grid = unsigned(tiles);
+    hipError_t err;
+    switch (world) {
+    case 1: err = launch_probe<1>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    case 2: err = launch_probe<2>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    case 4: err = launch_probe<4>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    case 8: err = launch_probe<8>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    case 16: err = launch_probe<16>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    case 32: err = launch_probe<32>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    default:
+        g_err = "synth_stream_probe_dev: world must be 1, 2, 4, 8, 16 or 32";
+        return -1;
+    }
+    return err == hipSuccess ? 0 : fail("stream probe launch", err);
 }
 
 int synth_spin_dev(double microseconds, void *stream)

@@ -70,3 +70,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_stream_probe_rejects_bad_arguments_without_a_gpu():
+    """The W-stream HBM probe checks its arguments before any HIP call."""
+    import synth
+    for kind, world, tiles, k in ((3, 8, 1, 0), (0, 3, 1, 0), (0, 8, -1, 0), (0, 8, 1, 9), (0, 8, 1 << 31, 0)):
+        with pytest.raises(RuntimeError, match="synth_stream_probe_dev"):
+            synth.stream_probe_dev(kind, world, 1 << 20, 1 << 20, 1 << 20, tiles, k)
+    with pytest.raises(RuntimeError, match="table"):
+        synth.stream_probe_dev(synth.PROBE_COPY, 8, 0, 1 << 20, 1 << 20, 1, 0)
+    synth.stream_probe_dev(synth.PROBE_COPY, 8, 1 << 20, 1 << 20, 1 << 20, 0, 0)   # nothing to do
