@@ -94,7 +94,7 @@ def unused_table(wl, frac: float, global_frac: float, seed: int = 2024):
 
 class Session:
     def __init__(self, wl, arena: bool = False, stagger=None, backward_kind: str = "spin", used=None,
-                 streams=None):
+                 streams=None, slots: bool = False):
         import numpy as np
         import torch
 
@@ -112,7 +112,7 @@ class Session:
         t0 = time.perf_counter()
         from synth.device import REPLICA_STAGGER
         self.stagger = REPLICA_STAGGER if stagger is None else stagger
-        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena, stagger=self.stagger)
+        self.inputs = DeviceInputs(wl, flat_off, self.total, arena=arena, stagger=self.stagger, slots=slots)
         log(f"[bench] inputs resident: {self.inputs.nbytes() / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
         self.compute, self.comm = streams if streams is not None else (torch.cuda.Stream(), torch.cuda.Stream())
         self.used = used
@@ -355,12 +355,12 @@ def run_stream_probe(args):
     """HBM rate of W equal-offset streams at the reduction's launch shape (one
     4 KiB tile of every buffer per 256-thread workgroup): W reads, W writes,
     or a copy of W buffers to W others, for W = 1 ... 32, at one and two
-    workgroups per CU and uncapped. These kernels move data and compute
+    workgroups per CU and uncapped, in the replica layout --layout names. These kernels move data and compute
     nothing: they measure what the access pattern itself reaches on this GPU,
     the ceiling the reduction's fold and stores sit under. One JSON line per W."""
     import torch
     import synth
-    from synth.device import REPLICA_STAGGER
+    from synth.device import REPLICA_STAGGER, replica_slot_bytes
     stagger = REPLICA_STAGGER if args.stagger is None else args.stagger
     if stagger < 0 or stagger % 256:
         raise SystemExit("--stream-probe needs a stagger that is a multiple of 256 bytes")
@@ -368,13 +368,25 @@ def run_stream_probe(args):
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
 
-    def buffers(n, nbytes):
-        # buffer k starts k * stagger bytes into its allocation, as the
-        # harness places replicas
-        held = [torch.full(((nbytes + n * stagger) // 4,), 0.5, dtype=torch.float32, device="cuda")
-                for _ in range(n)]
-        ptrs = [h.data_ptr() + k * stagger for k, h in enumerate(held)]
-        return held, torch.tensor(ptrs, dtype=torch.int64, device="cuda")
+    def buffers(n, nbytes, pair):
+        """n buffers of nbytes (two sets when pair), placed as the harness
+        places replicas: buffer k starts k * stagger bytes into its place,
+        which is slot k of one allocation (the second set at the slots'
+        middle) with the slot layout, else an allocation of its own."""
+        if args.layout == "slots":
+            slot = replica_slot_bytes(nbytes + n * stagger, nbytes + n * stagger if pair else 0)
+            arena = torch.full((n * slot // 4,), 0.5, dtype=torch.float32, device="cuda")
+            a0 = arena.data_ptr()
+            src = [a0 + k * slot + k * stagger for k in range(n)]
+            dst = [a0 + k * slot + slot // 2 + k * stagger for k in range(n)]
+            held = [arena]
+        else:
+            held = [torch.full(((nbytes + n * stagger) // 4,), 0.5, dtype=torch.float32, device="cuda")
+                    for _ in range(2 * n if pair else n)]
+            src = [h.data_ptr() + k * stagger for k, h in enumerate(held[:n])]
+            dst = [h.data_ptr() + k * stagger for k, h in enumerate(held[n:])]
+        tab = lambda ptrs: torch.tensor(ptrs, dtype=torch.int64, device="cuda") if ptrs else None
+        return held, tab(src), tab(dst)
 
     def rate(kind, W, src, dst, tiles, k, nbytes, reps=10):
         run = lambda: synth.stream_probe_dev(kind, W, src, dst, sink.data_ptr(), tiles, k, st.cuda_stream)
@@ -389,21 +401,21 @@ def run_stream_probe(args):
         return round(nbytes / (e0.elapsed_time(e1) / reps) / 1e6, 1)
 
     for W in (1, 2, 4, 8, 16, 32):
-        row = {"stream_probe": True, "W": W, "stagger": stagger, "bytes_per_pass": total,
+        row = {"stream_probe": True, "W": W, "layout": args.layout, "stagger": stagger, "bytes_per_pass": total,
                "read_GBps": {}, "write_GBps": {}, "copy_GBps": {}}
         size = total // W // 4096 * 4096
-        held, tab = buffers(W, size)
+        held, tab, _ = buffers(W, size, False)
         for k in (1, 2, 0):
             row["read_GBps"][str(k)] = rate(synth.PROBE_READ, W, tab.data_ptr(), 0, size // 4096, k, W * size)
             row["write_GBps"][str(k)] = rate(synth.PROBE_WRITE, W, 0, tab.data_ptr(), size // 4096, k, W * size)
         del held, tab
+        torch.cuda.empty_cache()
         size = total // (2 * W) // 4096 * 4096
-        hs, ts = buffers(W, size)
-        hd, td = buffers(W, size)
+        held, ts, td = buffers(W, size, True)
         for k in (1, 2, 0):
             row["copy_GBps"][str(k)] = rate(synth.PROBE_COPY, W, ts.data_ptr(), td.data_ptr(), size // 4096, k,
                                             2 * W * size)
-        del hs, ts, hd, td
+        del held, ts, td
         torch.cuda.empty_cache()
         print(json.dumps(row), flush=True)
 
@@ -426,7 +438,8 @@ def run_sweep(args):
     for W in worlds:
         for cap in caps:
             wl = wls.sweep(W, cap)
-            s = Session(wl, backward_kind=args.backward_kind, streams=streams)
+            s = Session(wl, backward_kind=args.backward_kind, streams=streams, slots=args.layout == "slots",
+                        arena=args.layout == "arena", stagger=args.stagger)
             import bucketed_gradient_all_amd as ddp
             ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
             nbytes = wl.algorithmic_bytes()
@@ -497,8 +510,11 @@ def main():
                     help="unused-parameter detection: each gradient unused on every replica with this probability")
     ap.add_argument("--no-scrub", action="store_true",
                     help="skip the extra event-timed pass that overwrites a 512 MiB buffer before each step")
-    ap.add_argument("--arena", action="store_true",
-                    help="carve every replica buffer out of one allocation instead of one allocation per buffer")
+    ap.add_argument("--layout", default="slots", choices=["slots", "separate", "arena"],
+                    help="replica buffers: slot w of one allocation per replica w (slots of a power of two, at "
+                         "least 4 GiB), one allocation per buffer (separate), or packed back to back in one "
+                         "allocation (arena)")
+    ap.add_argument("--arena", action="store_true", help="same as --layout arena")
     ap.add_argument("--stagger", type=int, default=None,
                     help="bytes by which replica w's buffers start w * stagger into their allocations "
                          "(default: synth.device.REPLICA_STAGGER)")
@@ -525,6 +541,8 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this size (for HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.arena:
+        args.layout = "arena"
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -581,13 +599,15 @@ def main():
         wl.name += f"_unused{args.unused_frac:g}_{args.unused_global_frac:g}"
     log(f"[bench] workload {wl.name}: P={len(wl.numel)} elements={wl.total_numel} W={wl.world} "
         f"mode={MODE_NAMES[wl.input_mode]}")
-    s = Session(wl, arena=args.arena, stagger=args.stagger, backward_kind=args.backward_kind, used=used)
+    s = Session(wl, arena=args.layout == "arena", stagger=args.stagger, backward_kind=args.backward_kind, used=used,
+                slots=args.layout == "slots")
     import bucketed_gradient_all_amd as ddp
     ddp.ddp_register_builtin_hook(s.r, hook)
     ddp.ddp_set_workgroups_per_cu(s.r, args.workgroups_per_cu)
     bytes_per_step = sum(bucket_alg_of(s, wl))
     launch_lds = ddp.ddp_get_launch_lds(s.r)
     stagger = s.stagger
+    slot_gib = s.inputs.slot_bytes >> 30
 
     for _ in range(args.warmup):
         s.step()
@@ -682,15 +702,15 @@ def main():
         torch.cuda.synchronize()
         cpu = cpu_baseline(wl, s, args.cpu_baseline_seconds, hook, used)
 
-    # The same launches with the replicas' buffers laid out plainly (no
-    # stagger: replica w's buffers at the start of their allocations), in a
-    # second set of buffers: the rate a caller gets without the placement
-    # the harness uses (see synth.device.REPLICA_STAGGER).
+    # The same launches with the replicas' buffers laid out plainly (one
+    # allocation per buffer, no stagger: replica w's buffers at the start of
+    # same-size allocations), in a second set of buffers: the rate a caller
+    # gets without the placement the harness uses (see synth.device).
     plain = None
-    if not args.no_plain_layout and s.stagger != 0:
+    if not args.no_plain_layout and (s.stagger != 0 or args.layout != "separate"):
         streams = (s.compute, s.comm)
         s.close()
-        ps = Session(wl, arena=args.arena, stagger=0, backward_kind=args.backward_kind, used=used, streams=streams)
+        ps = Session(wl, stagger=0, backward_kind=args.backward_kind, used=used, streams=streams)
         ddp.ddp_register_builtin_hook(ps.r, hook)
         ddp.ddp_set_workgroups_per_cu(ps.r, args.workgroups_per_cu)
         for _ in range(max(args.warmup, 3)):
@@ -702,12 +722,13 @@ def main():
         ddp.ddp_set_timing(ps.r, False)
         pbytes = sum(sum(bucket_alg[f:f + c]) for f, c in zip(pfirst, pcount))
         prate = pbytes / (float(pms.sum()) / 1e3) / 1e9 if pms.size else 0.0
-        plain = {"replica_stagger_bytes": 0, "achieved": round(prate, 1), "frac": round(prate / HBM_PEAK_GBPS, 4),
+        plain = {"replica_layout": "separate", "replica_stagger_bytes": 0, "achieved": round(prate, 1),
+                 "frac": round(prate / HBM_PEAK_GBPS, 4),
                  "launches": int(pms.size)}
         ps.close()
 
     # the committed counters describe the default launch and layout only
-    default_setup = args.workgroups_per_cu == 0 and args.stagger is None and not args.arena
+    default_setup = args.workgroups_per_cu == 0 and args.stagger is None and args.layout == "slots"
     traffic = measured_traffic(wl.name) if default_setup else None
     out = {
         "metric": METRIC,
@@ -732,6 +753,7 @@ def main():
                        "unused_pairs": int((used == 0).sum()),
                        "gradients_unused_everywhere": int((~used.any(axis=0)).sum())},
                    "workgroups_per_cu": args.workgroups_per_cu,
+                   "replica_layout": args.layout if args.layout != "slots" else f"slots of {slot_gib} GiB",
                    "replica_stagger_bytes": stagger,
                    "launch_lds_bytes": launch_lds,
                    "parallelism": "1 GPU, W replicas in HBM"},

@@ -29,13 +29,35 @@ ALIGN = 256
 # have. Replica w's buffers therefore start w * REPLICA_STAGGER bytes into
 # their allocations (a multiple of 256, so alignment is unchanged).
 REPLICA_STAGGER = 12288
+
+# The slot layout: replica w's gradients and flat buffer sit in slot w of one
+# allocation, gradients at the slot's start and the flat buffer at its middle,
+# with slots a power of two of at least 4 GiB. Measured on MI355X, W streams
+# at equal offsets in such slots run at a steadier and mostly higher rate
+# than in allocations packed back to back (W = 32: +15-19%, W = 16: +4%,
+# W = 8: +1-3%); the W copies of an element then differ in address bits 32
+# and up, as W separate memories would not collide at all.
+REPLICA_SLOT_MIN = 4 << 30
+
+
+def replica_slot_bytes(grad_bytes: int, flat_bytes: int) -> int:
+    """Slot size of the slot layout: the smallest power of two, at least
+    REPLICA_SLOT_MIN, whose halves hold one replica's gradient area and its
+    flat buffer (each already including that replica's stagger)."""
+    half = max(int(grad_bytes), int(flat_bytes), 1)
+    slot = REPLICA_SLOT_MIN
+    while slot // 2 < half:
+        slot *= 2
+    return slot
+
+
 SENTINEL = -1   # 0xFFFFFFFF: a NaN pattern the reduction never produces from finite inputs
 
 
 class DeviceInputs:
     def __init__(self, wl: Workload, flat_offset_elems: Sequence[int], total_elems: int, device: str = "cuda",
                  seed: Optional[int] = None, misalign: int = 0, flat_shift: int = 0, arena: bool = False,
-                 stagger: int = REPLICA_STAGGER):
+                 stagger: int = REPLICA_STAGGER, slots: bool = False):
         """misalign: bytes added to the start of every other gradient tensor
         (to exercise unaligned sources); flat_shift: elements the flat
         buffers start past their allocation, one value or one per replica (to
@@ -46,7 +68,9 @@ class DeviceInputs:
         flat buffers start w * stagger past their allocations, so that the W
         replicas' copies of one element do not sit at the same offset in
         same-size allocations (the HBM channel a line maps to depends on its
-        address); see REPLICA_STAGGER."""
+        address); see REPLICA_STAGGER;
+        slots: one allocation of W slots (see REPLICA_SLOT_MIN), replica w's
+        buffers in slot w, each still w * stagger past its slot half."""
         import torch
 
         self.wl = wl
@@ -76,7 +100,24 @@ class DeviceInputs:
         shifts = [sh + w * stagger // 4 for w, sh in enumerate(shifts)]
         self.flat_shift = shifts
         flat_bytes = (4 * (max(self.total, 1) + max(shifts)) + ALIGN - 1) // ALIGN * ALIGN
-        if arena:
+        self.slot_bytes = 0
+        if slots and arena:
+            raise ValueError("choose one of arena and slots")
+        if slots:
+            gb = self.grad_bytes + (W - 1) * stagger if self.mode != IN_F32_VIEW else 0
+            slot = replica_slot_bytes(gb, flat_bytes)
+            free, _ = torch.cuda.mem_get_info()
+            if W * slot > free:
+                raise MemoryError(f"the slot layout needs {W} x {slot >> 30} GiB; {free >> 30} GiB are free")
+            self.slot_bytes = slot
+            self._arena = torch.empty(W * slot, dtype=torch.uint8, device=device)
+            half = slot // 2
+            if gb:
+                self.grads = [self._arena[w * slot + w * stagger:w * slot + w * stagger + self.grad_bytes]
+                              for w in range(W)]
+            self._flat_alloc = [self._arena[w * slot + half:w * slot + half + flat_bytes].view(torch.float32)
+                                for w in range(W)]
+        elif arena:
             gb = self.grad_bytes + (W - 1) * stagger if self.mode != IN_F32_VIEW else 0
             self._arena = torch.empty(W * (gb + flat_bytes), dtype=torch.uint8, device=device)
             base = 0

@@ -81,3 +81,22 @@ def test_stream_probe_rejects_bad_arguments_without_a_gpu():
     with pytest.raises(RuntimeError, match="table"):
         synth.stream_probe_dev(synth.PROBE_COPY, 8, 0, 1 << 20, 1 << 20, 1, 0)
     synth.stream_probe_dev(synth.PROBE_COPY, 8, 1 << 20, 1 << 20, 1 << 20, 0, 0)   # nothing to do
+
+
+def test_replica_slot_size():
+    """Slots are a power of two of at least 4 GiB whose halves hold one
+    replica's gradient area and flat buffer."""
+    from synth.device import REPLICA_SLOT_MIN, replica_slot_bytes
+    G = 1 << 30
+    assert REPLICA_SLOT_MIN == 4 * G
+    assert replica_slot_bytes(0, 0) == 4 * G
+    assert replica_slot_bytes(2 * G, 2 * G) == 4 * G
+    assert replica_slot_bytes(2 * G + 1, 0) == 8 * G
+    assert replica_slot_bytes(0, 2 * G + 1) == 8 * G
+    # Megatron Llama-1B at W = 16: 1.9 GB of bf16 wgrads, 3.8 GB of fp32 main_grad per replica
+    wl = wls.megatron_llama1b()
+    flat = 4 * wl.total_numel + 16 * 12288
+    assert replica_slot_bytes(2 * wl.total_numel + 16 * 12288, flat) == 8 * G
+    for n in (5, 100, 3 * G, 17 * G):
+        s = replica_slot_bytes(n, n // 2)
+        assert s & (s - 1) == 0 and s // 2 >= n and (s == 4 * G or s // 4 < n)
