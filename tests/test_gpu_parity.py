@@ -34,7 +34,7 @@ class Run:
     """Device inputs + reducer for a workload, on two torch streams."""
 
     def __init__(self, wl, misalign=0, flat_shift=0, seed=None, same_stream=False, collective=0,
-                 find_unused=False):
+                 find_unused=False, slots=False):
         torch = _torch()
         import bucketed_gradient_all_amd as ddp
         from synth.device import DeviceInputs
@@ -45,7 +45,8 @@ class Run:
         flat_off = [int(bucket_flat[self.plan.bucket_of[p]] + self.plan.offset_in_bucket[p]) // 4
                     for p in range(len(wl.numel))]
         total = sum(bb) // 4
-        self.inputs = DeviceInputs(wl, flat_off, total, seed=seed, misalign=misalign, flat_shift=flat_shift)
+        self.inputs = DeviceInputs(wl, flat_off, total, seed=seed, misalign=misalign, flat_shift=flat_shift,
+                                   slots=slots)
         self.compute = torch.cuda.Stream()
         self.comm = self.compute if same_stream else torch.cuda.Stream()
         self.r = ddp.make_reducer(wl.world, wl.numel, self.plan, wl.input_mode, self.inputs.grad_ptrs(),
@@ -370,6 +371,21 @@ def test_resnet50_full_bit_exact():
     run.step()
     want = expected_flat(wl, oracle_plan(wl), wl.seed, nthreads=host_threads())
     assert_bits(run.flat_host(0), want, "resnet50 replica 0")
+    assert run.replicas_equal_device()
+    run.close()
+
+
+def test_resnet50_full_bit_exact_in_the_bench_layout():
+    """The replica slot layout bench.py times (8 slots of 4 GiB): same bits."""
+    from synth import workloads as wls
+    from expect import expected_flat, host_threads, oracle_plan
+    wl = wls.resnet50()
+    say("resnet50 in 4 GiB replica slots: generating and reducing")
+    run = Run(wl, slots=True)
+    assert run.inputs.slot_bytes == 4 << 30
+    run.step()
+    want = expected_flat(wl, oracle_plan(wl), wl.seed, nthreads=host_threads())
+    assert_bits(run.flat_host(0), want, "resnet50 replica 0 (slots)")
     assert run.replicas_equal_device()
     run.close()
 
