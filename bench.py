@@ -354,8 +354,10 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0, used=None):
 def run_stream_probe(args):
     """HBM rate of W equal-offset streams at the reduction's launch shape (one
     4 KiB tile of every buffer per 256-thread workgroup): W reads, W writes,
-    or a copy of W buffers to W others, for W = 1 ... 32, at one and two
-    workgroups per CU and uncapped, in the replica layout --layout names. These kernels move data and compute
+    a copy of W buffers to W others, or the bf16 -> fp32 accumulate pattern
+    (W 16-bit reads, W fp32 reads and in-place writes), for W = 1 ... 32, at
+    one and two workgroups per CU and uncapped, in the replica layout
+    --layout names. These kernels move data and compute
     nothing: they measure what the access pattern itself reaches on this GPU,
     the ceiling the reduction's fold and stores sit under. One JSON line per W."""
     import torch
@@ -388,8 +390,9 @@ def run_stream_probe(args):
         tab = lambda ptrs: torch.tensor(ptrs, dtype=torch.int64, device="cuda") if ptrs else None
         return held, tab(src), tab(dst)
 
-    def rate(kind, W, src, dst, tiles, k, nbytes, reps=10):
-        run = lambda: synth.stream_probe_dev(kind, W, src, dst, sink.data_ptr(), tiles, k, st.cuda_stream)
+    def rate(kind, W, src, dst, tiles, k, nbytes, reps=10, aux=0):
+        run = lambda: synth.stream_probe_dev(kind, W, src, dst, sink.data_ptr(), tiles, k, st.cuda_stream,
+                                             aux_table=aux)
         for _ in range(3):
             run()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,7 +405,7 @@ def run_stream_probe(args):
 
     for W in (1, 2, 4, 8, 16, 32):
         row = {"stream_probe": True, "W": W, "layout": args.layout, "stagger": stagger, "bytes_per_pass": total,
-               "read_GBps": {}, "write_GBps": {}, "copy_GBps": {}}
+               "read_GBps": {}, "write_GBps": {}, "copy_GBps": {}, "accum_GBps": {}}
         size = total // W // 4096 * 4096
         held, tab, _ = buffers(W, size, False)
         for k in (1, 2, 0):
@@ -416,6 +419,18 @@ def run_stream_probe(args):
             row["copy_GBps"][str(k)] = rate(synth.PROBE_COPY, W, ts.data_ptr(), td.data_ptr(), size // 4096, k,
                                             2 * W * size)
         del held, ts, td
+        torch.cuda.empty_cache()
+        # the bf16 -> fp32 accumulate pattern: per buffer pair, a 16-bit
+        # buffer of half the size is read and the fp32 buffer read and
+        # rewritten in place (10 bytes per element, as the reduction's
+        # DDP_IN_BF16_ACCUM_F32 mode); 16-bit buffers first, as the harness
+        # places gradients before the flat buffers
+        size = (2 * total // (5 * W)) // 4096 * 4096
+        held, ta, tx = buffers(W, size, True)
+        for k in (1, 2, 0):
+            row["accum_GBps"][str(k)] = rate(synth.PROBE_ACCUM, W, tx.data_ptr(), 0, size // 4096, k,
+                                             W * size * 5 // 2, aux=ta.data_ptr())
+        del held, ta, tx
         torch.cuda.empty_cache()
         print(json.dumps(row), flush=True)
 

@@ -90,7 +90,8 @@ def dev_lib():
         L.synth_copy_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.synth_stream_probe_dev.restype = ctypes.c_int
         L.synth_stream_probe_dev.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_void_p]
         L.synth_spin_dev.restype = ctypes.c_int
         L.synth_spin_dev.argtypes = [ctypes.c_double, ctypes.c_void_p]
         L.synth_last_error.restype = ctypes.c_char_p
@@ -161,15 +162,16 @@ def copy_dev(dst: int, src: int, nbytes: int, stream: int = 0) -> None:
         raise RuntimeError(dev_lib().synth_last_error().decode())
 
 
-PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
+PROBE_READ, PROBE_WRITE, PROBE_COPY, PROBE_ACCUM = 0, 1, 2, 3
 
 
 def stream_probe_dev(kind: int, world: int, src_table: int, dst_table: int, sink: int, tiles: int,
-                     workgroups_per_cu: int, stream: int = 0) -> None:
+                     workgroups_per_cu: int, stream: int = 0, aux_table: int = 0) -> None:
     """Enqueues one HBM-rate probe over `world` equal-offset buffers (see
-    synth.h): read (PROBE_READ), write (PROBE_WRITE) or copy (PROBE_COPY)."""
-    rc = dev_lib().synth_stream_probe_dev(kind, world, src_table, dst_table, sink, tiles, workgroups_per_cu,
-                                          stream)
+    synth.h): read (PROBE_READ), write (PROBE_WRITE), copy (PROBE_COPY) or
+    the bf16-into-fp32 accumulate pattern (PROBE_ACCUM, with aux_table)."""
+    rc = dev_lib().synth_stream_probe_dev(kind, world, src_table, dst_table, aux_table, sink, tiles,
+                                          workgroups_per_cu, stream)
     if rc != 0:
         raise RuntimeError(dev_lib().synth_last_error().decode())
 

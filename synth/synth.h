@@ -78,11 +78,15 @@ int synth_copy_dev(void *dst, const void *src, int64_t bytes, void *stream);
  * (every buffer holds tiles * 4096 bytes, 16-byte aligned). kind 0 reads the
  * sources (sink: a device array of 256 uint32 that is written only if a
  * loaded word pattern is all ones), 1 writes the destinations, 2 copies
- * source k to destination k. workgroups_per_cu (0..8; 0 = no cap) bounds the
- * workgroups resident per CU the way the reduction does, with reserved LDS.
- * Enqueued on `stream`; returns -1 on bad arguments or a launch error. */
-int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const void *dst_table, void *sink,
-                           int64_t tiles, int32_t workgroups_per_cu, void *stream);
+ * source k to destination k, 3 reads the sources and the 16-bit buffers of
+ * aux_table (tiles * 2048 bytes each, 8-byte aligned) and writes the sources
+ * back in place: the byte pattern of accumulating bf16 wgrads into fp32
+ * main_grad. Tables a kind does not use may be NULL. workgroups_per_cu
+ * (0..8; 0 = no cap) bounds the workgroups resident per CU the way the
+ * reduction does, with reserved LDS. Enqueued on `stream`; returns -1 on bad
+ * arguments or a launch error. */
+int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const void *dst_table,
+                           const void *aux_table, void *sink, int64_t tiles, int32_t workgroups_per_cu, void *stream);
 /* One workgroup that waits `microseconds` of wall-clock time on the device
  * (at most 10 s); a stand-in for a slice of backward compute. */
 int synth_spin_dev(double microseconds, void *stream);

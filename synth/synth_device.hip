@@ -94,17 +94,38 @@ __global__ __launch_bounds__(256) void copy_kernel(float4 *__restrict__ dst, con
 // reduction's launch shape. KIND 0 reads the W sources (the loaded words are
 // OR-ed and compared with a pattern the probe's fill never produces, so the
 // loads stay live; nothing is stored), KIND 1 writes a constant to the W
-// destinations, KIND 2 copies source k to destination k. Nontemporal loads
-// and stores, as in the reduction.
+// destinations, KIND 2 copies source k to destination k, KIND 3 is the
+// byte pattern of accumulating bf16 wgrads into fp32 main_grad: it reads a
+// 2 KiB tile of W 16-bit buffers (aux, kept live like KIND 0) and the W fp32
+// sources, and writes the fp32 values back in place. Nontemporal loads and
+// stores, as in the reduction.
 typedef float probe_f4 __attribute__((ext_vector_type(4)));
 typedef unsigned probe_u4 __attribute__((ext_vector_type(4)));
+typedef unsigned probe_u2 __attribute__((ext_vector_type(2)));
 
 template <int W, int KIND>
 __global__ __launch_bounds__(256) void stream_probe_kernel(const probe_f4 *const *__restrict__ src,
                                                            probe_f4 *const *__restrict__ dst,
+                                                           const probe_u2 *const *__restrict__ aux,
                                                            unsigned *__restrict__ sink)
 {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (KIND == 3) {
+        probe_f4 v[W];
+        probe_u2 h[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            v[k] = __builtin_nontemporal_load(src[k] + i);
+            h[k] = __builtin_nontemporal_load(aux[k] + i);
+        }
+        unsigned bits = 0;
+#pragma unroll
+        for (int k = 0; k < W; ++k) bits |= h[k].x & h[k].y;
+        if (bits == 0xFFFFFFFFu) sink[threadIdx.x] = bits;
+#pragma unroll
+        for (int k = 0; k < W; ++k) __builtin_nontemporal_store(v[k], const_cast<probe_f4 *>(src[k]) + i);
+        return;
+    }
     if (KIND == 1) {
         const probe_f4 c = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
@@ -126,15 +147,17 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const probe_f4 *const
 }
 
 template <int W>
-hipError_t launch_probe(int kind, const void *src, const void *dst, void *sink, unsigned grid, unsigned lds,
-                        hipStream_t st)
+hipError_t launch_probe(int kind, const void *src, const void *dst, const void *aux, void *sink, unsigned grid,
+                        unsigned lds, hipStream_t st)
 {
     const auto *s = static_cast<const probe_f4 *const *>(src);
     auto *d = static_cast<probe_f4 *const *>(const_cast<void *>(dst));
+    const auto *a = static_cast<const probe_u2 *const *>(aux);
     auto *k = static_cast<unsigned *>(sink);
-    if (kind == 0) hipLaunchKernelGGL((stream_probe_kernel<W, 0>), dim3(grid), dim3(256), lds, st, s, d, k);
-    else if (kind == 1) hipLaunchKernelGGL((stream_probe_kernel<W, 1>), dim3(grid), dim3(256), lds, st, s, d, k);
-    else hipLaunchKernelGGL((stream_probe_kernel<W, 2>), dim3(grid), dim3(256), lds, st, s, d, k);
+    if (kind == 0) hipLaunchKernelGGL((stream_probe_kernel<W, 0>), dim3(grid), dim3(256), lds, st, s, d, a, k);
+    else if (kind == 1) hipLaunchKernelGGL((stream_probe_kernel<W, 1>), dim3(grid), dim3(256), lds, st, s, d, a, k);
+    else if (kind == 2) hipLaunchKernelGGL((stream_probe_kernel<W, 2>), dim3(grid), dim3(256), lds, st, s, d, a, k);
+    else hipLaunchKernelGGL((stream_probe_kernel<W, 3>), dim3(grid), dim3(256), lds, st, s, d, a, k);
     return hipGetLastError();
 }
 
@@ -224,11 +247,12 @@ int synth_copy_dev(void *dst, const void *src, int64_t bytes, void *stream)
     return err == hipSuccess ? 0 : fail("copy launch", err);
 }
 
-int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const void *dst_table, void *sink,
-                           int64_t tiles, int32_t workgroups_per_cu, void *stream)
+int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const void *dst_table,
+                           const void *aux_table, void *sink, int64_t tiles, int32_t workgroups_per_cu, void *stream)
 {
-    if (kind < 0 || kind > 2 || tiles < 0 || tiles > int64_t(0x7FFFFFFF) || workgroups_per_cu < 0 ||
-        workgroups_per_cu > 8 || (kind != 1 && (!src_table || !sink)) || (kind != 0 && !dst_table)) {
+    if (kind < 0 || kind > 3 || tiles < 0 || tiles > int64_t(0x7FFFFFFF) || workgroups_per_cu < 0 ||
+        workgroups_per_cu > 8 || (kind != 1 && (!src_table || !sink)) || ((kind == 1 || kind == 2) && !dst_table) ||
+        (kind == 3 && !aux_table)) {
         g_err = "synth_stream_probe_dev: bad kind, tile count, cap or table";
         return -1;
     }
@@ -251,12 +275,12 @@ int synth_stream_probe_dev(int kind, int32_t world, const void *src_table, const
     const unsigned grid = unsigned(tiles);
     hipError_t err;
     switch (world) {
-    case 1: err = launch_probe<1>(kind, src_table, dst_table, sink, grid, lds, st); break;
-    case 2: err = launch_probe<2>(kind, src_table, dst_table, sink, grid, lds, st); break;
-    case 4: err = launch_probe<4>(kind, src_table, dst_table, sink, grid, lds, st); break;
-    case 8: err = launch_probe<8>(kind, src_table, dst_table, sink, grid, lds, st); break;
-    case 16: err = launch_probe<16>(kind, src_table, dst_table, sink, grid, lds, st); break;
-    case 32: err = launch_probe<32>(kind, src_table, dst_table, sink, grid, lds, st); break;
+    case 1: err = launch_probe<1>(kind, src_table, dst_table, aux_table, sink, grid, lds, st); break;
+    case 2: err = launch_probe<2>(kind, src_table, dst_table, aux_table, sink, grid, lds, st); break;
+    case 4: err = launch_probe<4>(kind, src_table, dst_table, aux_table, sink, grid, lds, st); break;
+    case 8: err = launch_probe<8>(kind, src_table, dst_table, aux_table, sink, grid, lds, st); break;
+    case 16: err = launch_probe<16>(kind, src_table, dst_table, aux_table, sink, grid, lds, st); break;
+    case 32: err = launch_probe<32>(kind, src_table, dst_table, aux_table, sink, grid, lds, st); break;
     default:
         g_err = "synth_stream_probe_dev: world must be 1, 2, 4, 8, 16 or 32";
         return -1;

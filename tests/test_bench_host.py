@@ -75,7 +75,8 @@ def test_more_than_one_gpu_is_refused():
 def test_stream_probe_rejects_bad_arguments_without_a_gpu():
     """The W-stream HBM probe checks its arguments before any HIP call."""
     import synth
-    for kind, world, tiles, k in ((3, 8, 1, 0), (0, 3, 1, 0), (0, 8, -1, 0), (0, 8, 1, 9), (0, 8, 1 << 31, 0)):
+    for kind, world, tiles, k in ((4, 8, 1, 0), (0, 3, 1, 0), (0, 8, -1, 0), (0, 8, 1, 9), (0, 8, 1 << 31, 0),
+                                  (3, 8, 1, 0)):   # the accumulate pattern without its 16-bit table
         with pytest.raises(RuntimeError, match="synth_stream_probe_dev"):
             synth.stream_probe_dev(kind, world, 1 << 20, 1 << 20, 1 << 20, tiles, k)
     with pytest.raises(RuntimeError, match="table"):
