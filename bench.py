@@ -261,14 +261,18 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0, used=None):
     import synth
     from oracle import compress, fold
     from oracle.plan import plan_buckets
-    from synth.workloads import IN_BF16_ACCUM_F32, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD
+    from synth.workloads import IN_BF16_ACCUM_F32, REDUCE_SCATTER, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD
 
     oplan = plan_buckets(wl.param_bytes, wl.order_mode, cap=wl.cap_bytes, first_cap=wl.first_cap_bytes)
-    per_elem = 10 if wl.input_mode == IN_BF16_ACCUM_F32 else 8
+    # algorithmic bytes per element of the workload's collective: every
+    # replica's input read, the sum written to every replica (all-reduce) or
+    # to the chunk's owner (reduce-scatter); the oracle computes the same sums
+    read = 6 if wl.input_mode == IN_BF16_ACCUM_F32 else 4
+    per_elem = read * wl.world + (4 if wl.collective == REDUCE_SCATTER else 4 * wl.world)
     budget_bytes = 2.0e9          # algorithmic bytes of the sample (bounded host memory)
     chosen, acc = [], 0
     for b in range(oplan.n_buckets):
-        nb = per_elem * wl.world * oplan.bucket_bytes[b] // 4
+        nb = per_elem * oplan.bucket_bytes[b] // 4
         if chosen and acc + nb > budget_bytes:
             break
         chosen.append(b)
@@ -325,24 +329,33 @@ def cpu_baseline(wl, session, target_s: float, hook: int = 0, used=None):
     gbps_1 = acc / t1 / 1e9
     gbps_mt = acc * reps_mt / tmt / 1e9
     match = None
-    if session is not None and wl.collective == 0:
+    if session is not None:
         match = True
+        rs = wl.collective == REDUCE_SCATTER
         for b, out in zip(chosen, outs):
             lo = sum(oplan.bucket_bytes[:b]) // 4
-            got = session.inputs.flat[0][lo:lo + out.size].cpu().numpy()
             written = np.ones(out.size, bool)
             if used is not None:      # gradients no replica used keep their contents
                 for p in oplan.buckets[b]:
                     if not any(used[w][p] for w in range(wl.world)):
                         o = oplan.offset_in_bucket[p] // 4
                         written[o:o + wl.numel[p]] = False
-            match &= bool(np.array_equal(got.view(np.uint32)[written], out.view(np.uint32)[written]))
+            # all-reduce: replica 0 holds every sum; reduce-scatter: chunk c
+            # (q = ceil(n / W) elements) is stored to replica c only
+            q = -(-out.size // wl.world) if rs else out.size
+            for c in range(wl.world if rs else 1):
+                a, e = min(c * q, out.size), min((c + 1) * q, out.size)
+                if a == e:
+                    continue
+                got = session.inputs.flat[c][lo + a:lo + e].cpu().numpy()
+                match &= bool(np.array_equal(got.view(np.uint32)[written[a:e]], out[a:e].view(np.uint32)[written[a:e]]))
     n_elems = sum(oplan.bucket_bytes[b] for b in chosen) // 4
     return {
         "value": round(gbps_mt, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"buckets 0..{chosen[-1]} of {oplan.n_buckets} ({n_elems} elements x W={wl.world}, "
                   f"{acc / 1e9:.2f} GB algorithmic), threaded fold x{reps_mt}; inputs regenerated on the host, "
                   f"generation untimed",
+        "sample_bytes": int(acc),
         "single_thread_value": round(gbps_1, 3),
         "cpu_seconds": round(t1 + tmt, 2),
         "cpu_model": host_cpu_model(),

@@ -101,3 +101,17 @@ def test_replica_slot_size():
     for n in (5, 100, 3 * G, 17 * G):
         s = replica_slot_bytes(n, n // 2)
         assert s & (s - 1) == 0 and s // 2 >= n and (s == 4 * G or s // 4 < n)
+
+
+@pytest.mark.parametrize("collective", [0, 1])
+def test_cpu_baseline_counts_the_collectives_bytes(collective):
+    """The oracle leg of bench.py on the tiny workload without a GPU session:
+    its sample's algorithmic bytes are the collective's (4W read + 4W written
+    per element for the all-reduce, 4W + 4 for the reduce-scatter)."""
+    wl = wls.tiny()
+    wl.collective = collective
+    r = bench.cpu_baseline(wl, None, 0.05)
+    n = wl.total_numel
+    want = (4 * wl.world + (4 if collective else 4 * wl.world)) * n
+    assert r["sample_bytes"] == want and r["value"] > 0
+    assert r["gpu_matches_oracle_on_sample"] is None and r["kind"] == "oracle"
