@@ -102,6 +102,19 @@ __global__ __launch_bounds__(256) void copy_kernel(float4 *__restrict__ dst, con
 typedef float probe_f4 __attribute__((ext_vector_type(4)));
 typedef unsigned probe_u4 __attribute__((ext_vector_type(4)));
 typedef unsigned probe_u2 __attribute__((ext_vector_type(2)));
+#define PROBE_GLOBAL __attribute__((address_space(1)))   // global-memory instructions, as the reduction uses
+
+template <class T>
+__device__ __forceinline__ T probe_ld(const T *p)
+{
+    return __builtin_nontemporal_load((const PROBE_GLOBAL T *)(p));
+}
+
+template <class T>
+__device__ __forceinline__ void probe_st(T v, T *p)
+{
+    __builtin_nontemporal_store(v, (PROBE_GLOBAL T *)(p));
+}
 
 template <int W, int KIND>
 __global__ __launch_bounds__(256) void stream_probe_kernel(const probe_f4 *const *__restrict__ src,
@@ -115,29 +128,35 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const probe_f4 *const
         probe_u2 h[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) {
-            v[k] = __builtin_nontemporal_load(src[k] + i);
-            h[k] = __builtin_nontemporal_load(aux[k] + i);
+            v[k] = probe_ld(src[k] + i);
+            h[k] = probe_ld(aux[k] + i);
         }
         unsigned bits = 0;
 #pragma unroll
         for (int k = 0; k < W; ++k) bits |= h[k].x & h[k].y;
         if (bits == 0xFFFFFFFFu) sink[threadIdx.x] = bits;
 #pragma unroll
-        for (int k = 0; k < W; ++k) __builtin_nontemporal_store(v[k], const_cast<probe_f4 *>(src[k]) + i);
+        for (int k = 0; k < W; ++k) {
+            // an empty asm that claims to change v[k]: without it the
+            // compiler may drop the store of a value just loaded from the
+            // same address, and the probe would write nothing
+            asm volatile("" : "+v"(v[k]));
+            probe_st(v[k], const_cast<probe_f4 *>(src[k]) + i);
+        }
         return;
     }
     if (KIND == 1) {
         const probe_f4 c = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
-        for (int k = 0; k < W; ++k) __builtin_nontemporal_store(c, dst[k] + i);
+        for (int k = 0; k < W; ++k) probe_st(c, dst[k] + i);
         return;
     }
     probe_f4 v[W];
 #pragma unroll
-    for (int k = 0; k < W; ++k) v[k] = __builtin_nontemporal_load(src[k] + i);
+    for (int k = 0; k < W; ++k) v[k] = probe_ld(src[k] + i);
     if (KIND == 2) {
 #pragma unroll
-        for (int k = 0; k < W; ++k) __builtin_nontemporal_store(v[k], dst[k] + i);
+        for (int k = 0; k < W; ++k) probe_st(v[k], dst[k] + i);
         return;
     }
     probe_u4 bits = {0u, 0u, 0u, 0u};
