@@ -7,10 +7,10 @@
 namespace ddp {
 
 hipError_t launch_mean(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                       int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s)
+                       int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, bool pair, hipStream_t s)
 {
     if (n_tiles <= 0) return hipSuccess;
-    return dispatch_mode<HOOK_MEAN>(mode, W, reduce_scatter, t, tile_begin, n_tiles, sc, lds_bytes, s);
+    return dispatch_mode<HOOK_MEAN>(mode, W, reduce_scatter, t, tile_begin, n_tiles, sc, lds_bytes, s, pair);
 }
 
 }  // namespace ddp

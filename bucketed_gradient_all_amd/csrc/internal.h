@@ -32,6 +32,14 @@ constexpr int unroll_for(int W, bool reduce_scatter, bool bf16_accum)
     return (W == 2 || W >= 5) ? 1 : 4;
 }
 
+// Whether an instance has a two-tile form (two consecutive tiles per
+// workgroup): the all-reduce instances with small tiles (one vector group per
+// thread) that the automatic cap runs two per CU, W = 5 to 8.
+constexpr bool pairs_tiles(int W, bool reduce_scatter, bool partial, bool bf16_accum)
+{
+    return !reduce_scatter && !partial && W >= 5 && W <= 8 && unroll_for(W, reduce_scatter, bf16_accum) == 1;
+}
+
 // Elements one workgroup covers (one tile).
 constexpr int64_t tile_elems(int W, bool reduce_scatter, bool bf16_accum)
 {
@@ -84,12 +92,14 @@ struct Scale {
 //   launch_bf16_hook:  through the bf16 compression hook
 //   launch_fp16_hook:  through the fp16 compression hook
 // lds_bytes: LDS each workgroup reserves (unused by the kernel; it bounds the
-// workgroups resident per CU).
+// workgroups resident per CU). pair: two consecutive tiles per workgroup, for
+// launches that run one workgroup per CU; only the instances that have that
+// form use it (pairs_tiles), the others ignore it.
 hipError_t launch_mean(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                       int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
+                       int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, bool pair, hipStream_t s);
 hipError_t launch_bf16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                            int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
+                            int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, bool pair, hipStream_t s);
 hipError_t launch_fp16_hook(int mode, int W, bool reduce_scatter, const Scale &sc, const KernelTables &t,
-                            int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, hipStream_t s);
+                            int32_t tile_begin, int32_t n_tiles, unsigned lds_bytes, bool pair, hipStream_t s);
 
 }  // namespace ddp

@@ -337,34 +337,47 @@ __device__ __forceinline__ void fold_scalar_fixed(const float *const (&xs)[W], c
 // tile gets an offset past every range and reads nothing either. The
 // instances that write through the L2 store the same way, over this tile of
 // each destination.
-template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED, bool PARTIAL>
-__device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
-                                            float *const (&ds)[NOUT], uint64_t on, const DeviceSeg &sg,
-                                            int64_t tin, const Scale &sc, Slots<W, PARTIAL> slots, bool write)
+//
+// The part is split in three steps (the lanes' offsets, the loads, the folds
+// and stores) so that a workgroup holding two tiles can issue both tiles'
+// loads before its first store.
+template <int U>
+struct TileLanes {
+    int64_t t0;          // the tile's first element
+    int64_t e[U];        // element of vector group u
+    int64_t el[U];       // the element a lane loads (in bounds also for lanes past the segment)
+    uint32_t rel[U];     // element offset from t0 (buffer loads and stores)
+    bool ok[U];          // vector group u lies inside the segment
+    uint32_t span;       // elements of the tile inside the segment
+};
+
+template <int U, bool CHECK>
+__device__ __forceinline__ TileLanes<U> tile_lanes(const DeviceSeg &sg, int64_t tin)
 {
-    constexpr int U = PARTIAL ? 1 : unroll_for(W, RS, MODE == MODE_BF16);
     constexpr int64_t TILE = int64_t(kThreads) * 4 * U;
-    constexpr int DIV = div_of<W, PARTIAL>();
     constexpr uint32_t kPast = 0x3FFFFFF0u;   // an element offset past every range (x4 bytes still fits)
     const int tid = int(threadIdx.x);
-    const int64_t t0 = sg.head + tin * TILE;   // the tile's first element
-    int64_t e[U], el[U];
-    uint32_t rel[U];   // element offset from t0 (buffer loads and stores)
-    bool ok[U];
+    TileLanes<U> L;
+    L.t0 = sg.head + tin * TILE;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t r = int64_t(u * kThreads + tid) * 4;
-        e[u] = t0 + r;
-        ok[u] = !CHECK || e[u] + 4 <= sg.len;
-        el[u] = ok[u] ? e[u] : int64_t(sg.head);   // the segment's first vector: in bounds
-        rel[u] = ok[u] ? uint32_t(r) : kPast;
+        L.e[u] = L.t0 + r;
+        L.ok[u] = !CHECK || L.e[u] + 4 <= sg.len;
+        L.el[u] = L.ok[u] ? L.e[u] : int64_t(sg.head);   // the segment's first vector: in bounds
+        L.rel[u] = L.ok[u] ? uint32_t(r) : kPast;
     }
     // elements of this tile inside the segment (the last tile may hold fewer,
     // or none past its head: t0 can exceed len by less than one vector group)
-    const uint32_t span = CHECK ? uint32_t(sg.len > t0 ? (sg.len - t0 < TILE ? sg.len - t0 : TILE) : 0)
-                                : uint32_t(TILE);
-    f32x4 v[U][W];
-    u16x4 g[U][W];
+    L.span = CHECK ? uint32_t(sg.len > L.t0 ? (sg.len - L.t0 < TILE ? sg.len - L.t0 : TILE) : 0) : uint32_t(TILE);
+    return L;
+}
+
+template <int W, int U, int MODE, bool USED, bool PARTIAL>
+__device__ __forceinline__ void vector_load(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
+                                            uint64_t on, const TileLanes<U> &L, Slots<W, PARTIAL> slots,
+                                            f32x4 (&v)[U][W], u16x4 (&g)[U][W])
+{
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         if (!slots.has(k)) {   // an absent slot: nothing to read
@@ -377,13 +390,13 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
         }
         if (USED) {
             const bool use = (on >> k) & 1;
-            const __amdgpu_buffer_rsrc_t rx = range_of(xs[k] + t0, use ? 4 * span : 0);
+            const __amdgpu_buffer_rsrc_t rx = range_of(xs[k] + L.t0, use ? 4 * L.span : 0);
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u][k] = ld4_in(rx, 4 * rel[u]);
+            for (int u = 0; u < U; ++u) v[u][k] = ld4_in(rx, 4 * L.rel[u]);
             if (MODE == MODE_BF16) {
-                const __amdgpu_buffer_rsrc_t rg = range_of(gs[k] + t0, use ? 2 * span : 0);
+                const __amdgpu_buffer_rsrc_t rg = range_of(gs[k] + L.t0, use ? 2 * L.span : 0);
 #pragma unroll
-                for (int u = 0; u < U; ++u) g[u][k] = ld4h_in(rg, 2 * rel[u]);
+                for (int u = 0; u < U; ++u) g[u][k] = ld4h_in(rg, 2 * L.rel[u]);
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) g[u][k] = u16x4{0, 0, 0, 0};
@@ -392,10 +405,18 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            v[u][k] = ld4(xs[k] + el[u]);
-            g[u][k] = MODE == MODE_BF16 ? ld4h(gs[k] + el[u]) : u16x4{0, 0, 0, 0};
+            v[u][k] = ld4(xs[k] + L.el[u]);
+            g[u][k] = MODE == MODE_BF16 ? ld4h(gs[k] + L.el[u]) : u16x4{0, 0, 0, 0};
         }
     }
+}
+
+template <int W, int NOUT, int U, int MODE, int HOOK, bool RS, bool PARTIAL>
+__device__ __forceinline__ void vector_fold_store(const f32x4 (&v)[U][W], const u16x4 (&g)[U][W],
+                                                  float *const (&ds)[NOUT], const TileLanes<U> &L,
+                                                  const Scale &sc, Slots<W, PARTIAL> slots, bool write)
+{
+    constexpr int DIV = div_of<W, PARTIAL>();
     f32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -408,32 +429,148 @@ __device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const u
         // through a buffer resource over this tile of each destination: the
         // lanes past the segment (offset past the range) and a gradient no
         // replica used (range 0) store nothing
-        const uint32_t range = write ? 4 * span : 0;
+        const uint32_t range = write ? 4 * L.span : 0;
 #pragma unroll
         for (int w = 0; w < NOUT; ++w) {
             if (!(NOUT == 1 || slots.has(w))) continue;   // an absent slot has no destination
-            const __amdgpu_buffer_rsrc_t rd = range_of(ds[w] + t0, range);
+            const __amdgpu_buffer_rsrc_t rd = range_of(ds[w] + L.t0, range);
 #pragma unroll
-            for (int u = 0; u < U; ++u) st4_in(rd, 4 * rel[u], acc[u]);
+            for (int u = 0; u < U; ++u) st4_in(rd, 4 * L.rel[u], acc[u]);
         }
     } else {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (ok[u] && write) {
+            if (L.ok[u] && write) {
 #pragma unroll
                 for (int w = 0; w < NOUT; ++w)
-                    if (NOUT == 1 || slots.has(w)) st4(ds[w] + e[u], acc[u]);
+                    if (NOUT == 1 || slots.has(w)) st4(ds[w] + L.e[u], acc[u]);
             }
+    }
+}
+
+template <int W, int NOUT, int MODE, int HOOK, bool RS, bool CHECK, bool USED, bool PARTIAL>
+__device__ __forceinline__ void vector_tile(const float *const (&xs)[W], const unsigned short *const (&gs)[W],
+                                            float *const (&ds)[NOUT], uint64_t on, const DeviceSeg &sg,
+                                            int64_t tin, const Scale &sc, Slots<W, PARTIAL> slots, bool write)
+{
+    constexpr int U = PARTIAL ? 1 : unroll_for(W, RS, MODE == MODE_BF16);
+    const TileLanes<U> L = tile_lanes<U, CHECK>(sg, tin);
+    f32x4 v[U][W];
+    u16x4 g[U][W];
+    vector_load<W, U, MODE, USED, PARTIAL>(xs, gs, on, L, slots, v, g);
+    vector_fold_store<W, NOUT, U, MODE, HOOK, RS, PARTIAL>(v, g, ds, L, sc, slots, write);
+}
+
+// Everything one tile needs before its first memory access: its segment, its
+// index inside it, the hoisted source and destination pointers, and the slot
+// mask. All table reads (segment, source and destination pointers) happen
+// here, before the first store, so they stay in scalar registers; a table
+// read after a store would have to go through the vector memory path and wait
+// for every outstanding store.
+template <int W, int NOUT>
+struct TileRefs {
+    DeviceSeg sg;
+    int64_t tin;
+    const float *xs[W];
+    const unsigned short *gs[W];
+    float *ds[NOUT];
+    uint64_t on;   // bit k: slot k contributes
+    bool write;    // false: no replica used the gradient, leave it untouched
+};
+
+template <int W, int NOUT, int MODE, bool RS, bool USED, bool PARTIAL>
+__device__ __forceinline__ void tile_refs(const KernelTables &T, int32_t tile, Slots<W, PARTIAL> slots,
+                                          TileRefs<W, NOUT> &t)
+{
+    const int nrep = slots.count();
+    t.sg = T.segs[T.tile_seg[tile]];
+    const DeviceSeg &sg = t.sg;
+    const uint64_t m = USED ? sg.used : ~uint64_t(0);
+    t.tin = int64_t(tile - sg.tile0);
+
+    // slot k holds replica (chunk + k) mod nrep, so the fold is slot 0, 1, ...
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        t.xs[k] = nullptr;
+        t.gs[k] = nullptr;
+        if (!slots.has(k)) continue;
+        const int r = slot_replica(sg.chunk, k, nrep);
+        t.xs[k] = src_f32<MODE>(T, sg, r);
+        t.gs[k] = MODE == MODE_BF16 ? src_bf16(T, sg, r) : nullptr;
+    }
+    if (MODE != MODE_COPY) {
+        // The sources are the flat buffers themselves (VIEW input, bf16-mode
+        // main_grad). Slot k reads replica (chunk + k) mod n, so slot 0 is the
+        // chunk's owner and the slots cover every replica once: the stores go
+        // through the source pointers, and no second set of W pointers takes
+        // scalar registers.
+#pragma unroll
+        for (int w = 0; w < NOUT; ++w) t.ds[w] = slots.has(w) ? const_cast<float *>(t.xs[w]) : nullptr;
+    } else if (RS) {
+        t.ds[0] = T.flat[sg.chunk] + sg.flat;   // chunk c belongs to replica c
+    } else {
+#pragma unroll
+        for (int w = 0; w < NOUT; ++w) t.ds[w] = slots.has(w) ? T.flat[w] + sg.flat : nullptr;
+    }
+
+    // No early exit when no replica used the gradient: a branch on the mask
+    // ahead of the loads lets the compiler fetch the mask chain first and the
+    // segment chain only after it (two more round trips per tile). With every
+    // replica's range empty nothing is read; the stores are skipped.
+    // Slot bits: bit k is set when slot k's replica, (chunk + k) mod n, used
+    // the gradient: the replica mask rotated into fold order (n <= 32 here).
+    // One 64-bit value instead of a flag per slot, which would take a scalar
+    // register pair each.
+    t.on = ~uint64_t(0);
+    t.write = true;
+    if (USED) {
+        t.write = m != 0;
+        const uint64_t full = (uint64_t(1) << nrep) - 1;
+        const uint64_t mm = m & full;
+        const int c = sg.chunk;
+        t.on = ((mm >> c) | (mm << (nrep - c))) & full;
+    }
+}
+
+// One tile: the vector body (whole or last tile of the segment), the first
+// tile's scalar head and tail, or a segment folded one element per lane.
+template <int W, int NOUT, int MODE, int HOOK, bool RS, bool USED, bool PARTIAL>
+__device__ __forceinline__ void run_tile(const TileRefs<W, NOUT> &t, const Scale &sc, Slots<W, PARTIAL> slots)
+{
+    constexpr int64_t TILE = PARTIAL ? int64_t(kThreads) * 4 : tile_elems(W, RS, MODE == MODE_BF16);
+    const DeviceSeg &sg = t.sg;
+    const int64_t tin = t.tin;
+    const int tid = int(threadIdx.x);
+    if (sg.head >= 0) {
+        if (sg.head + (tin + 1) * TILE <= sg.len)
+            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED, PARTIAL>(t.xs, t.gs, t.ds, t.on, sg, tin, sc, slots,
+                                                                       t.write);
+        else if (sg.len - sg.head >= 4)
+            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED, PARTIAL>(t.xs, t.gs, t.ds, t.on, sg, tin, sc, slots,
+                                                                      t.write);
+        if (tin == 0) {
+            const int64_t body = (sg.len - sg.head) / 4 * 4;
+            const int64_t tail = sg.len - sg.head - body;
+            if (tid < sg.head)
+                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(t.xs, t.gs, t.ds, t.on, tid, sc, slots,
+                                                                      t.write);
+            if (tid >= 64 && tid < 64 + tail)
+                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(t.xs, t.gs, t.ds, t.on,
+                                                                      sg.head + body + (tid - 64), sc, slots, t.write);
+        }
+        return;
+    }
+    for (int64_t j = tid; j < TILE; j += kThreads) {
+        const int64_t e = tin * TILE + j;
+        if (e < sg.len)
+            fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(t.xs, t.gs, t.ds, t.on, e, sc, slots, t.write);
     }
 }
 
 // W slots at compile time: fully unrolled over replicas and vector groups.
 // With PARTIAL, n replicas (n <= W, known at run time) fill the first n
 // slots and the tiles are 4 elements per thread (the host's tiling for every
-// replica count these instances serve). All table reads (segment, source and
-// destination pointers) happen before the first store, so they stay in
-// scalar registers; a table read after a store would have to go through the
-// vector memory path and wait for every outstanding store.
+// replica count these instances serve).
 //
 // Waves per SIMD an instance is compiled for: the most the automatic cap
 // lets share a SIMD. The 32-slot instances run at most two workgroups per CU
@@ -458,81 +595,50 @@ void reduce_fixed(
     KernelTables T, int32_t tile_begin, Scale sc, int n)
 {
     constexpr int NOUT = RS ? 1 : W;
-    constexpr int64_t TILE = PARTIAL ? int64_t(kThreads) * 4 : tile_elems(W, RS, MODE == MODE_BF16);
     const Slots<W, PARTIAL> slots{n};
-    const int nrep = slots.count();
-    const int32_t tile = tile_begin + int32_t(blockIdx.x);
-    const DeviceSeg sg = T.segs[T.tile_seg[tile]];
-    const uint64_t m = USED ? sg.used : ~uint64_t(0);
-    const int64_t tin = int64_t(tile - sg.tile0);
+    TileRefs<W, NOUT> t;
+    tile_refs<W, NOUT, MODE, RS, USED, PARTIAL>(T, tile_begin + int32_t(blockIdx.x), slots, t);
+    run_tile<W, NOUT, MODE, HOOK, RS, USED, PARTIAL>(t, sc, slots);
+}
 
-    // slot k holds replica (chunk + k) mod nrep, so the fold is slot 0, 1, ...
-    const float *xs[W];
-    const unsigned short *gs[W];
-    float *ds[NOUT];
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-        xs[k] = nullptr;
-        gs[k] = nullptr;
-        if (!slots.has(k)) continue;
-        const int r = slot_replica(sg.chunk, k, nrep);
-        xs[k] = src_f32<MODE>(T, sg, r);
-        gs[k] = MODE == MODE_BF16 ? src_bf16(T, sg, r) : nullptr;
-    }
-    if (MODE != MODE_COPY) {
-        // The sources are the flat buffers themselves (VIEW input, bf16-mode
-        // main_grad). Slot k reads replica (chunk + k) mod n, so slot 0 is the
-        // chunk's owner and the slots cover every replica once: the stores go
-        // through the source pointers, and no second set of W pointers takes
-        // scalar registers.
-#pragma unroll
-        for (int w = 0; w < NOUT; ++w) ds[w] = slots.has(w) ? const_cast<float *>(xs[w]) : nullptr;
-    } else if (RS) {
-        ds[0] = T.flat[sg.chunk] + sg.flat;   // chunk c belongs to replica c
-    } else {
-#pragma unroll
-        for (int w = 0; w < NOUT; ++w) ds[w] = slots.has(w) ? T.flat[w] + sg.flat : nullptr;
-    }
-
-    // No early exit when no replica used the gradient: a branch on the mask
-    // ahead of the loads lets the compiler fetch the mask chain first and the
-    // segment chain only after it (two more round trips per tile). With every
-    // replica's range empty nothing is read; the stores are skipped.
-    // Slot bits: bit k is set when slot k's replica, (chunk + k) mod n, used
-    // the gradient: the replica mask rotated into fold order (n <= 32 here).
-    // One 64-bit value instead of a flag per slot, which would take a scalar
-    // register pair each.
-    uint64_t on = ~uint64_t(0);
-    bool write = true;
-    if (USED) {
-        write = m != 0;   // no replica used this gradient: leave it untouched
-        const uint64_t full = (uint64_t(1) << nrep) - 1;
-        const uint64_t mm = m & full;
-        const int c = sg.chunk;
-        on = ((mm >> c) | (mm << (nrep - c))) & full;
-    }
-
-    const int tid = int(threadIdx.x);
-    if (sg.head >= 0) {
-        if (sg.head + (tin + 1) * TILE <= sg.len)
-            vector_tile<W, NOUT, MODE, HOOK, RS, false, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots, write);
-        else if (sg.len - sg.head >= 4)
-            vector_tile<W, NOUT, MODE, HOOK, RS, true, USED, PARTIAL>(xs, gs, ds, on, sg, tin, sc, slots, write);
-        if (tin == 0) {
-            const int64_t body = (sg.len - sg.head) / 4 * 4;
-            const int64_t tail = sg.len - sg.head - body;
-            if (tid < sg.head)
-                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, tid, sc, slots, write);
-            if (tid >= 64 && tid < 64 + tail)
-                fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, sg.head + body + (tid - 64),
-                                                                      sc, slots, write);
-        }
+// Two consecutive tiles per workgroup, for launches that run one workgroup
+// per CU with a small-tile instance (beside a running backward): the same
+// bytes in flight per CU as two single-tile workgroups, in half as many
+// workgroups, which leaves the backward's kernels more room. Both tiles'
+// tables are read first; when both tiles are whole vector tiles (the common
+// case), the second tile's loads go out before the first tile's stores, else
+// the two run one after the other. tile_end bounds the launch: the last
+// workgroup of an odd count holds one tile.
+template <int W, int MODE, int HOOK, bool USED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 8)))
+void reduce_pair(KernelTables T, int32_t tile_begin, int32_t tile_end, Scale sc)
+{
+    static_assert(pairs_tiles(W, false, false, MODE == MODE_BF16), "no two-tile form");
+    constexpr int U = 1;
+    constexpr int64_t TILE = tile_elems(W, false, MODE == MODE_BF16);
+    const Slots<W, false> slots{W};
+    const int32_t first = tile_begin + 2 * int32_t(blockIdx.x);
+    const bool two = first + 1 < tile_end;
+    TileRefs<W, W> a, b;
+    tile_refs<W, W, MODE, false, USED, false>(T, first, slots, a);
+    if (two) tile_refs<W, W, MODE, false, USED, false>(T, first + 1, slots, b);
+    // a whole vector tile with no scalar head or tail to fold
+    auto whole = [](const TileRefs<W, W> &t) {
+        return t.sg.head >= 0 && t.tin != 0 && t.sg.head + (t.tin + 1) * TILE <= t.sg.len;
+    };
+    if (two && whole(a) && whole(b)) {
+        const TileLanes<U> la = tile_lanes<U, false>(a.sg, a.tin);
+        const TileLanes<U> lb = tile_lanes<U, false>(b.sg, b.tin);
+        f32x4 va[U][W], vb[U][W];
+        u16x4 ga[U][W], gb[U][W];
+        vector_load<W, U, MODE, USED, false>(a.xs, a.gs, a.on, la, slots, va, ga);
+        vector_load<W, U, MODE, USED, false>(b.xs, b.gs, b.on, lb, slots, vb, gb);
+        vector_fold_store<W, W, U, MODE, HOOK, false, false>(va, ga, a.ds, la, sc, slots, a.write);
+        vector_fold_store<W, W, U, MODE, HOOK, false, false>(vb, gb, b.ds, lb, sc, slots, b.write);
         return;
     }
-    for (int64_t j = tid; j < TILE; j += kThreads) {
-        const int64_t e = tin * TILE + j;
-        if (e < sg.len) fold_scalar_fixed<W, NOUT, MODE, HOOK, USED, PARTIAL>(xs, gs, ds, on, e, sc, slots, write);
-    }
+    run_tile<W, W, MODE, HOOK, false, USED, false>(a, sc, slots);
+    if (two) run_tile<W, W, MODE, HOOK, false, USED, false>(b, sc, slots);
 }
 
 // Any W the fixed and partial instances do not serve (above 32): replicas are
@@ -587,12 +693,26 @@ __global__ __launch_bounds__(kThreads) void reduce_generic(KernelTables T, int32
     scalar_parts<MODE, HOOK>(T, sg, m, tin, TILE, sc, W, rs != 0);
 }
 
-// n: the replica count (at most W; below W only with PARTIAL).
+// n: the replica count (at most W; below W only with PARTIAL). pair: two
+// tiles per workgroup where the instance has that form (pairs_tiles), else
+// ignored.
 template <int W, int MODE, int HOOK, bool PARTIAL>
 hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc, bool rs,
-                        unsigned lds, hipStream_t st, int n)
+                        unsigned lds, hipStream_t st, int n, bool pair)
 {
-    const dim3 g(n_tiles), b(kThreads);
+    const dim3 b(kThreads);
+    if constexpr (pairs_tiles(W, false, PARTIAL, MODE == MODE_BF16)) {
+        if (pair && !rs) {
+            const dim3 g2((unsigned(n_tiles) + 1) / 2);
+            const int32_t tile_end = tile_begin + n_tiles;
+            if (t.masked)
+                hipLaunchKernelGGL((reduce_pair<W, MODE, HOOK, true>), g2, b, lds, st, t, tile_begin, tile_end, sc);
+            else
+                hipLaunchKernelGGL((reduce_pair<W, MODE, HOOK, false>), g2, b, lds, st, t, tile_begin, tile_end, sc);
+            return hipGetLastError();
+        }
+    }
+    const dim3 g(n_tiles);
     if (t.masked) {
         if (rs)
             hipLaunchKernelGGL((reduce_fixed<W, MODE, HOOK, true, true, PARTIAL>), g, b, lds, st, t, tile_begin, sc, n);
@@ -612,27 +732,27 @@ hipError_t launch_fixed(const KernelTables &t, int32_t tile_begin, int32_t n_til
 
 template <int MODE, int HOOK>
 hipError_t dispatch_w(int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles, const Scale &sc,
-                      unsigned lds, hipStream_t st)
+                      unsigned lds, hipStream_t st, bool pair)
 {
     switch (W) {
-    case 1: return launch_fixed<1, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 2: return launch_fixed<2, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 3: return launch_fixed<3, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 4: return launch_fixed<4, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 5: return launch_fixed<5, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 6: return launch_fixed<6, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 7: return launch_fixed<7, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 8: return launch_fixed<8, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 16: return launch_fixed<16, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
-    case 32: return launch_fixed<32, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+    case 1: return launch_fixed<1, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 2: return launch_fixed<2, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 3: return launch_fixed<3, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 4: return launch_fixed<4, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 5: return launch_fixed<5, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 6: return launch_fixed<6, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 7: return launch_fixed<7, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 8: return launch_fixed<8, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 16: return launch_fixed<16, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
+    case 32: return launch_fixed<32, MODE, HOOK, false>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
     default:
         // the partial instances tile 4 elements per thread, as the host does
         // for every replica count between 9 and 31 (checked, so that a change
         // of the tiling rule falls back to the generic kernel)
         if (W > 8 && W < 16 && unroll_for(W, rs, MODE == MODE_BF16) == 1)
-            return launch_fixed<16, MODE, HOOK, true>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+            return launch_fixed<16, MODE, HOOK, true>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
         if (W > 16 && W < 32 && unroll_for(W, rs, MODE == MODE_BF16) == 1)
-            return launch_fixed<32, MODE, HOOK, true>(t, tile_begin, n_tiles, sc, rs, lds, st, W);
+            return launch_fixed<32, MODE, HOOK, true>(t, tile_begin, n_tiles, sc, rs, lds, st, W, pair);
         hipLaunchKernelGGL((reduce_generic<MODE, HOOK>), dim3(n_tiles), dim3(kThreads), lds, st, t, tile_begin, sc,
                            W, rs ? 1 : 0);
         return hipGetLastError();
@@ -641,12 +761,12 @@ hipError_t dispatch_w(int W, bool rs, const KernelTables &t, int32_t tile_begin,
 
 template <int HOOK>
 hipError_t dispatch_mode(int mode, int W, bool rs, const KernelTables &t, int32_t tile_begin, int32_t n_tiles,
-                         const Scale &sc, unsigned lds, hipStream_t st)
+                         const Scale &sc, unsigned lds, hipStream_t st, bool pair)
 {
     switch (mode) {
-    case MODE_COPY: return dispatch_w<MODE_COPY, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st);
-    case MODE_VIEW: return dispatch_w<MODE_VIEW, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st);
-    case MODE_BF16: return dispatch_w<MODE_BF16, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st);
+    case MODE_COPY: return dispatch_w<MODE_COPY, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st, pair);
+    case MODE_VIEW: return dispatch_w<MODE_VIEW, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st, pair);
+    case MODE_BF16: return dispatch_w<MODE_BF16, HOOK>(W, rs, t, tile_begin, n_tiles, sc, lds, st, pair);
     default: return hipErrorInvalidValue;
     }
 }

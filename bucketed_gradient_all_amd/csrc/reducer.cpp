@@ -288,24 +288,38 @@ struct ddp_reducer {
     int32_t workgroups_per_cu = 0;               // 0: automatic, < 0: no cap, 1..8: cap
     int lds_per_cu = 0, lds_per_block = 0;       // the device's LDS sizes (bytes)
 
-    // set while a launch is issued beside a running backward (the compute
-    // stream has work of the caller's queued; see issue_buckets)
+    // set while a launch is issued beside a running backward (see
+    // issue_buckets)
     bool beside_backward = false;
 
-    // LDS each launch reserves so that at most k of its workgroups share a CU.
-    // Beside a running backward the automatic rule allows one workgroup per
-    // CU, which leaves the backward's kernels most of each CU's LDS and
-    // wave slots; the exposed tail gets the rule tuned for bandwidth.
-    unsigned launch_lds() const
+    // Workgroups of the next launch resident per CU (0: no cap). Beside a
+    // running backward the automatic rule allows one workgroup per CU, which
+    // leaves the backward's kernels most of each CU's LDS and wave slots; the
+    // exposed tail gets the rule tuned for bandwidth.
+    int launch_k() const
     {
         int k = workgroups_per_cu == 0 ? auto_workgroups_per_cu(pv.W, pv.reduce_scatter,
                                                                  pv.mode == DDP_IN_BF16_ACCUM_F32)
                                        : (workgroups_per_cu < 0 ? 0 : workgroups_per_cu);
         if (workgroups_per_cu == 0 && beside_backward && k > 1) k = 1;
+        return k;
+    }
+    // LDS each launch reserves so that at most k of its workgroups share a CU.
+    unsigned launch_lds() const
+    {
+        const int k = launch_k();
         if (k <= 0 || lds_per_cu <= 0) return 0;
         int bytes = lds_per_cu / (k + 1) + 2048;   // k fit, k + 1 do not
         bytes = (bytes + 255) / 256 * 256;
         return unsigned(std::min(bytes, lds_per_block));
+    }
+    // At one workgroup per CU the small-tile instances (W = 5..8 all-reduce)
+    // give each workgroup two tiles, so that a CU keeps the bytes in flight
+    // of the two workgroups their tuned rule allows.
+    bool launch_pair() const
+    {
+        return launch_k() == 1 && lds_per_cu > 0 &&
+               ddp::pairs_tiles(pv.W, pv.reduce_scatter, false, pv.mode == DDP_IN_BF16_ACCUM_F32);
     }
     KernelTables tables{};
     // tables in the static area of this device (ddp_reducer_create_static),
@@ -319,11 +333,6 @@ struct ddp_reducer {
     // ev_ready keeps the default system-scope release: with device scope the
     // HIP runtime made every launch of a many-launch step about 20 us slower.
     hipEvent_t ev_ready = nullptr, ev_done = nullptr, ev_host = nullptr;
-    // ev_fin: recorded on the compute stream right behind finish's wait for
-    // the comm stream; until it completes, work queued on the compute stream
-    // may be nothing but that wait
-    hipEvent_t ev_fin = nullptr;
-    bool fin_recorded = false;
     // unused detection: ev_tables orders a reduction on another stream after
     // the segment-table upload on the comm stream; ev_foreign orders later
     // uploads after that reduction
@@ -521,16 +530,17 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
     const int32_t tile0 = r->pv.tile_begin[b0];
     const int32_t tiles = r->pv.tile_begin[b1 - 1] + r->pv.tile_count[b1 - 1] - tile0;
     const unsigned lds = r->launch_lds();
+    const bool pair = r->launch_pair();
     const PlanView &pv = r->pv;
     switch (r->builtin_hook) {
     case DDP_HOOK_BF16_COMPRESS:
-        e = ddp::launch_bf16_hook(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
+        e = ddp::launch_bf16_hook(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, pair, s);
         break;
     case DDP_HOOK_FP16_COMPRESS:
-        e = ddp::launch_fp16_hook(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
+        e = ddp::launch_fp16_hook(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, pair, s);
         break;
     default:
-        e = ddp::launch_mean(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, s);
+        e = ddp::launch_mean(pv.mode, pv.W, pv.reduce_scatter, r->scale, r->tables, tile0, tiles, lds, pair, s);
         break;
     }
     if (e != hipSuccess) {
@@ -591,13 +601,15 @@ int issue_buckets(ddp_reducer *r, int32_t b0, int32_t b1, int32_t *at)
     if (r->device && r->compute != r->comm) {
         hipError_t e = hipStreamQuery(r->compute);
         if (e == hipErrorNotReady) {
-            // The compute stream has work queued: the caller's backward, or
-            // only the wait the last ddp_finish left there (back-to-back
-            // reductions). The wait is behind ev_fin, so once ev_fin is done
-            // whatever is still queued is the caller's.
-            hipError_t q = r->fin_recorded ? hipEventQuery(r->ev_fin) : hipSuccess;
-            if (q != hipSuccess && q != hipErrorNotReady) return hip_fail("stream query", q);
-            r->beside_backward = q == hipSuccess;
+            // The compute stream has work queued. A launch that does not hold
+            // the backward's last bucket runs beside the backward kernels
+            // still to come [PTD-notes §2.2.3], which compete with it for the
+            // CUs: it takes the shape for that. The last launch waits for the
+            // backward's final kernels and then runs alone (the exposed tail):
+            // it takes the shape tuned for bandwidth. Whether the queued work
+            // is a backward or only the wait the last ddp_finish left there,
+            // HIP cannot tell; a backward is the case that matters.
+            r->beside_backward = b1 < r->pv.B;
             e = hipEventRecord(r->ev_ready, r->compute);
             if (e == hipSuccess) e = hipStreamWaitEvent(r->comm, r->ev_ready, 0);
         }
@@ -695,8 +707,6 @@ void destroy_events(ddp_reducer *r) noexcept
     if (r->ev_ready) (void)hipEventDestroy(r->ev_ready);
     if (r->ev_done) (void)hipEventDestroy(r->ev_done);
     if (r->ev_host) (void)hipEventDestroy(r->ev_host);
-    if (r->ev_fin) (void)hipEventDestroy(r->ev_fin);
-    r->ev_fin = nullptr;
     if (r->ev_tables) (void)hipEventDestroy(r->ev_tables);
     if (r->ev_foreign) (void)hipEventDestroy(r->ev_foreign);
     r->ev_tables = r->ev_foreign = nullptr;
@@ -931,8 +941,6 @@ int create_reducer(const ddp_reducer_desc *desc, ddp_reducer **out, bool static_
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&r->ev_done, hipEventDisableTiming | hipEventDisableSystemFence);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&r->ev_host, hipEventDisableTiming);
-        if (e == hipSuccess)
-            e = hipEventCreateWithFlags(&r->ev_fin, hipEventDisableTiming | hipEventDisableSystemFence);
         if (e == hipSuccess && pv.find_unused && !pv.segs.empty()) {
             e = hipHostMalloc(reinterpret_cast<void **>(&r->stage), 2 * sizeof(DeviceSeg) * pv.segs.size());
             for (int k = 0; k < 2 && e == hipSuccess; ++k)
@@ -1076,8 +1084,6 @@ int ddp_finish_impl(ddp_reducer *r, int32_t host_blocking)
         if (r->compute != r->comm) {
             e = hipEventRecord(r->ev_done, r->comm);
             if (e == hipSuccess) e = hipStreamWaitEvent(r->compute, r->ev_done, 0);
-            if (e == hipSuccess) e = hipEventRecord(r->ev_fin, r->compute);
-            if (e == hipSuccess) r->fin_recorded = true;
         }
         if (e == hipSuccess && host_blocking) {
             e = hipEventRecord(r->ev_host, r->comm);

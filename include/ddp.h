@@ -354,24 +354,30 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
  * LDS; a launch reserves LDS only so that the hardware dispatcher keeps at
  * most n of its workgroups on a CU. Fewer tiles in flight keep the 2W
  * streams' windows narrow, which suits HBM: on MI355X this measured 2-8%
- * faster than full occupancy for 3 <= W <= 32. The reserved LDS is
- * unavailable to kernels that share the CUs: with bf16 GEMMs running beside
- * the reduction as the backward, BERT-large's overlapped step was about
- * 0.6 ms (3%) shorter at n = 1 than at the automatic two per CU, so a caller
- * whose backward kernels need LDS may prefer n = 1, or no cap.
+ * faster than full occupancy for 3 <= W <= 32. The reserved LDS and the
+ * wave slots are unavailable to kernels that share the CUs, such as the
+ * backward's GEMMs.
  *   n = 0  automatic (default): none for W <= 2 and for W > 32; two per CU
  *          for the reduce-scatter and for the all-reduce at W = 5..32;
  *          except that the all-reduce at W = 3, 4 runs one per CU (none in
  *          DDP_IN_BF16_ACCUM_F32 mode) and the DDP_IN_BF16_ACCUM_F32
- *          all-reduce at W = 16 runs one per CU. A launch issued while the
- *          caller's backward still has work queued on the compute stream
- *          [PTD-notes §2.2.3] runs at most one per CU, which leaves more of
- *          each CU to the backward's kernels (work queued there counts as the
- *          caller's once the wait that the last ddp_finish left on the
- *          compute stream is done; before that, as with back-to-back
- *          reductions, the launch keeps the rule above);
+ *          all-reduce at W = 16 runs one per CU. A launch of a managed
+ *          backward (ddp_mark_ready*) that does not hold the backward's last
+ *          bucket, issued while the compute stream has work queued, runs
+ *          beside the backward's remaining kernels [PTD-notes §2.2.3] and
+ *          takes at most one per CU; the last launch, which runs after the
+ *          backward's final kernels, keeps the rule above;
  *   n < 0  no cap (no LDS reserved; occupancy limited by registers only);
  *   1..8   at most n per CU.
+ * At one workgroup per CU (by either rule) the all-reduce at W = 5..8 gives
+ * each workgroup two consecutive tiles, so a CU keeps the bytes in flight of
+ * the two single-tile workgroups the automatic rule allows, in half the
+ * workgroups (BERT-large with bf16 GEMMs as its backward, MI355X: the
+ * overlapped step 1.26 ms shorter than the serial one, against 0.40-0.49 ms
+ * with two single-tile workgroups per CU beside the backward). A managed
+ * backward without backward kernels, such as back-to-back reductions marked
+ * one bucket at a time, cannot be told apart and takes the same shape: its
+ * launches ran 5-7% below the tuned rule.
  * The instance for the DDP_IN_BF16_ACCUM_F32 all-reduce at W = 16 is compiled
  * for one wave per SIMD (all of its loads in flight), so it holds one
  * workgroup per CU whatever n allows.

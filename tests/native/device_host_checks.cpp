@@ -370,36 +370,60 @@ void check_static_area()
 }
 
 // The occupancy rule of a launch: the tuned cap (two workgroups per CU at
-// W = 8) for back-to-back reductions and the exposed tail, one per CU beside
-// a running backward. A backward is taken to be running when the compute
-// stream has work queued and the wait that the last finish left there is
-// done (or there was no finish yet).
+// W = 8) for back-to-back reductions and for the launch that holds the
+// backward's last bucket (the exposed tail); one per CU, with two tiles per
+// workgroup, for the other launches of a backward while the compute stream
+// has work queued.
 void check_launch_occupancy()
 {
     fake::g_logging = true;
-    Model m(8, 12, 1 << 30, false, 41);   // one bucket: one launch per backward
+    Model m(8, 12, 6000, false, 41);   // several buckets: one launch per bucket
+    expect(m.B >= 3, "occupancy: the model has several buckets");
     ddp_reducer *r = nullptr;
     expect(ddp_reducer_create(&m.d, &r) == DDP_OK, "occupancy: create");
     int32_t tuned = 0;
     expect(ddp_get_launch_lds(r, &tuned) == DDP_OK && tuned == 56832, "occupancy: two per CU at W = 8");
-    auto launch_lds = [&]() -> long {
+    const unsigned one = 83968;   // one per CU
+    auto launches = [&](ddp_reducer *rr, const Model &mm) {
         fake::reset_log();
-        if (backward(r, m) != DDP_OK) return -1;
+        std::vector<fake::Call> v;
+        if (backward(rr, mm) != DDP_OK) return v;
         for (const auto &c : fake::g_log)
-            if (!std::strcmp(c.what, "launch")) return long(c.lds);
-        return -2;
+            if (!std::strcmp(c.what, "launch")) v.push_back(c);
+        return v;
     };
-    fake::g_stream_query = hipErrorNotReady;   // the caller's backward is queued; no finish yet
-    expect(launch_lds() == 83968, "occupancy: first backward beside queued work: one per CU");
-    fake::g_event_query = hipErrorNotReady;    // compute still waits for the last reduction
-    expect(launch_lds() == tuned, "occupancy: back-to-back reductions keep the tuned cap");
-    fake::g_event_query = hipSuccess;          // that wait is done: the queued work is a backward
-    expect(launch_lds() == 83968, "occupancy: beside a running backward: one per CU");
-    fake::g_stream_query = hipSuccess;         // compute drained: the exposed tail
-    expect(launch_lds() == tuned, "occupancy: drained compute stream keeps the tuned cap");
+    auto shape = [&](const std::vector<fake::Call> &v, unsigned lds_first, bool pair_first, unsigned lds_last,
+                     bool pair_last) {
+        if (v.size() != size_t(m.B)) return false;
+        for (size_t i = 0; i + 1 < v.size(); ++i)
+            if (v[i].lds != lds_first || v[i].pair != pair_first) return false;
+        return v.back().lds == lds_last && v.back().pair == pair_last;
+    };
+    fake::g_stream_query = hipErrorNotReady;   // the compute stream has work queued
+    expect(shape(launches(r, m), one, true, unsigned(tuned), false),
+           "occupancy: beside a backward one per CU with two tiles, the last launch tuned");
+    fake::g_stream_query = hipSuccess;         // compute drained: nothing runs beside
+    expect(shape(launches(r, m), unsigned(tuned), false, unsigned(tuned), false),
+           "occupancy: drained compute stream keeps the tuned cap");
     fake::g_stream_query = hipErrorNotReady;
-    expect(ddp_set_workgroups_per_cu(r, 2) == DDP_OK && launch_lds() == tuned, "occupancy: explicit cap kept");
+    expect(ddp_set_workgroups_per_cu(r, 2) == DDP_OK &&
+               shape(launches(r, m), unsigned(tuned), false, unsigned(tuned), false),
+           "occupancy: explicit cap of two kept beside a backward");
+    expect(ddp_set_workgroups_per_cu(r, 1) == DDP_OK && shape(launches(r, m), one, true, one, true),
+           "occupancy: explicit cap of one: two tiles per workgroup");
+    expect(ddp_set_workgroups_per_cu(r, -1) == DDP_OK && shape(launches(r, m), 0, false, 0, false),
+           "occupancy: no cap");
     expect(ddp_reducer_destroy(r) == DDP_OK, "occupancy: destroy");
+    // W = 16 (one vector group per thread, two per CU tuned) has no two-tile form
+    Model m16(16, 12, 6000, false, 42);
+    expect(ddp_reducer_create(&m16.d, &r) == DDP_OK, "occupancy: create W = 16");
+    fake::g_stream_query = hipErrorNotReady;
+    const auto v16 = launches(r, m16);
+    bool ok = v16.size() == size_t(m16.B) && !v16.empty();
+    for (size_t i = 0; ok && i < v16.size(); ++i) ok = !v16[i].pair && (i + 1 == v16.size()) == (v16[i].lds != one);
+    expect(ok, "occupancy: W = 16 beside a backward: one per CU, single tiles");
+    expect(ddp_reducer_destroy(r) == DDP_OK, "occupancy: destroy W = 16");
+    fake::g_stream_query = hipErrorNotReady;
 }
 
 }  // namespace

@@ -40,7 +40,7 @@ void log_call(Call c)
     if (g_logging) g_log.push_back(c);
 }
 
-hipError_t launch(const char *what, hipStream_t s, int32_t tile0, int32_t tiles, unsigned lds)
+hipError_t launch(const char *what, hipStream_t s, int32_t tile0, int32_t tiles, unsigned lds, bool pair)
 {
     Call c{};
     c.what = what;
@@ -48,6 +48,7 @@ hipError_t launch(const char *what, hipStream_t s, int32_t tile0, int32_t tiles,
     c.a = tile0;
     c.b = tiles;
     c.lds = lds;
+    c.pair = pair;
     log_call(c);
     return hipSuccess;
 }
@@ -226,21 +227,21 @@ uint64_t static_table_generation(int)
 }
 
 hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles,
-                       unsigned lds, hipStream_t s)
+                       unsigned lds, bool pair, hipStream_t s)
 {
-    return fake::launch("launch", s, tile0, tiles, lds);
+    return fake::launch("launch", s, tile0, tiles, lds, pair);
 }
 
 hipError_t launch_bf16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles,
-                            unsigned lds, hipStream_t s)
+                            unsigned lds, bool pair, hipStream_t s)
 {
-    return fake::launch("launch", s, tile0, tiles, lds);
+    return fake::launch("launch", s, tile0, tiles, lds, pair);
 }
 
 hipError_t launch_fp16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t tile0, int32_t tiles,
-                            unsigned lds, hipStream_t s)
+                            unsigned lds, bool pair, hipStream_t s)
 {
-    return fake::launch("launch", s, tile0, tiles, lds);
+    return fake::launch("launch", s, tile0, tiles, lds, pair);
 }
 
 }  // namespace ddp

@@ -14,6 +14,7 @@ struct Call {
     hipEvent_t event;     // record, wait, sync
     int64_t a, b;         // launch: first tile, tiles; copy: bytes
     unsigned lds;         // launch: LDS reserved per workgroup
+    bool pair;            // launch: two tiles per workgroup
 };
 
 extern std::vector<Call> g_log;

@@ -17,12 +17,13 @@ STUB = r'''
 #include "internal.h"
 #include "static_area.h"
 namespace ddp {
-hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned, hipStream_t)
+hipError_t launch_mean(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned, bool,
+                       hipStream_t)
 { return hipErrorInvalidValue; }
-hipError_t launch_bf16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned,
+hipError_t launch_bf16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned, bool,
                             hipStream_t)
 { return hipErrorInvalidValue; }
-hipError_t launch_fp16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned,
+hipError_t launch_fp16_hook(int, int, bool, const Scale &, const KernelTables &, int32_t, int32_t, unsigned, bool,
                             hipStream_t)
 { return hipErrorInvalidValue; }
 hipError_t static_table_area(int, void **, size_t *) { return hipErrorNoDevice; }
