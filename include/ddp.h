@@ -373,8 +373,9 @@ int ddp_register_builtin_hook(ddp_reducer *r, int32_t hook);
  * each workgroup two consecutive tiles, so a CU keeps the bytes in flight of
  * the two single-tile workgroups the automatic rule allows, in half the
  * workgroups (BERT-large with bf16 GEMMs as its backward, MI355X: the
- * overlapped step 1.26-1.35 ms shorter than the serial one, against 0.40-0.49 ms
- * with two single-tile workgroups per CU beside the backward). A managed
+ * overlapped step 0.92-1.58 ms shorter than the serial one, median 1.27 ms
+ * over six runs, against 0.40-0.49 ms with two single-tile workgroups per CU
+ * beside the backward). A managed
  * backward without backward kernels, such as back-to-back reductions marked
  * one bucket at a time, cannot be told apart and takes the same shape: its
  * launches ran 5-7% below the tuned rule.
