@@ -177,9 +177,11 @@ def ddp_last_error() -> str:
     return lib().ddp_last_error().decode()
 
 
-def _check(rc: int) -> int:
+def _check(rc: int, L=None) -> int:
+    """Raises DDPError for a failed call; L: the library that made the call
+    (its thread's last error text), the loaded one by default."""
     if rc < 0:
-        raise DDPError(rc, ddp_last_error())
+        raise DDPError(rc, (L or lib()).ddp_last_error().decode())
     return rc
 
 
@@ -296,7 +298,7 @@ class Reducer:
         self._hook = None
         self._hook_error: Optional[BaseException] = None
         self.workspace = None
-        self._lib = lib()   # the library that created the reducer destroys it
+        self._lib = lib()   # the library that created the reducer serves every call on it
         self._finalizer = weakref.finalize(self, _release, self._holder, [desc], self._lib)
 
     @property
@@ -314,7 +316,7 @@ class Reducer:
         hook raised becomes the cause of the DDPError."""
         err, self._hook_error = self._hook_error, None
         if rc < 0:
-            raise DDPError(rc, ddp_last_error()) from err
+            raise DDPError(rc, self._lib.ddp_last_error().decode()) from err
         return rc
 
 
@@ -340,22 +342,22 @@ def ddp_reducer_destroy(r: Reducer) -> None:
     if h:
         r._holder[0] = None
         r._finalizer.detach()
-        _check(r._lib.ddp_reducer_destroy(h))
+        _check(r._lib.ddp_reducer_destroy(h), r._lib)
 
 
 def ddp_prepare_for_backward(r: Reducer) -> None:
-    _check(lib().ddp_prepare_for_backward(r.handle))
+    _check(r._lib.ddp_prepare_for_backward(r.handle), r._lib)
 
 
 def ddp_mark_ready(r: Reducer, param: int) -> None:
-    r.check(lib().ddp_mark_ready(r.handle, param))
+    r.check(r._lib.ddp_mark_ready(r.handle, param))
 
 
 def ddp_mark_ready_many(r: Reducer, params) -> int:
     """Marks params in order; returns how many were marked (all, unless it raises)."""
     arr = np.ascontiguousarray(params, dtype=np.int32)
     done = ctypes.c_int32()
-    rc = lib().ddp_mark_ready_many(r.handle, arr.ctypes.data, arr.size, ctypes.byref(done))
+    rc = r._lib.ddp_mark_ready_many(r.handle, arr.ctypes.data, arr.size, ctypes.byref(done))
     try:
         r.check(rc)
     except DDPError as err:
@@ -365,7 +367,7 @@ def ddp_mark_ready_many(r: Reducer, params) -> int:
 
 
 def ddp_set_require_sync(r: Reducer, sync: bool) -> None:
-    _check(lib().ddp_set_require_sync(r.handle, 1 if sync else 0))
+    _check(r._lib.ddp_set_require_sync(r.handle, 1 if sync else 0), r._lib)
 
 
 def ddp_set_local_used(r: Reducer, used) -> None:
@@ -377,15 +379,15 @@ def ddp_set_local_used(r: Reducer, used) -> None:
     W, P = r.desc.c.world, r.desc.numel.size
     if arr.size != W * P:
         raise ValueError(f"used table must have {W}*{P} entries")
-    _check(lib().ddp_set_local_used(r.handle, arr.ctypes.data))
+    _check(r._lib.ddp_set_local_used(r.handle, arr.ctypes.data), r._lib)
 
 
 def ddp_bucket_reduce(r: Reducer, bucket: int, stream: int) -> None:
-    _check(lib().ddp_bucket_reduce(r.handle, bucket, stream or None))
+    _check(r._lib.ddp_bucket_reduce(r.handle, bucket, stream or None), r._lib)
 
 
 def ddp_finish(r: Reducer, host_blocking: bool = False) -> None:
-    r.check(lib().ddp_finish(r.handle, 1 if host_blocking else 0))
+    r.check(r._lib.ddp_finish(r.handle, 1 if host_blocking else 0))
 
 
 def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> None:
@@ -394,7 +396,7 @@ def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> No
     bucket, as a DDPError (DDP_ERR_HOOK) whose cause is that exception."""
     if fn is None:
         r._hook = None
-        _check(lib().ddp_register_comm_hook(r.handle, HOOK_FN(), None))
+        _check(r._lib.ddp_register_comm_hook(r.handle, HOOK_FN(), None), r._lib)
         return
 
     def call(ctx, b):
@@ -405,13 +407,14 @@ def ddp_register_comm_hook(r: Reducer, fn: Optional[Callable[[int], int]]) -> No
             return -1
 
     r._hook = HOOK_FN(call)
-    _check(lib().ddp_register_comm_hook(r.handle, r._hook, None))
+    _check(r._lib.ddp_register_comm_hook(r.handle, r._hook, None), r._lib)
 
 
 def ddp_set_bucket_groups(r: Reducer, first_buckets: Sequence[int]) -> None:
     """first_buckets: the first bucket of every group (empty: one group per bucket)."""
     arr = np.ascontiguousarray(np.asarray(list(first_buckets), dtype=np.int32))
-    _check(lib().ddp_set_bucket_groups(r.handle, arr.ctypes.data if arr.size else None, int(arr.size)))
+    _check(r._lib.ddp_set_bucket_groups(r.handle, arr.ctypes.data if arr.size else None, int(arr.size)),
+           r._lib)
 
 
 def groups_by_bytes(bucket_bytes: Sequence[int], min_group_bytes: int) -> List[int]:
@@ -427,57 +430,59 @@ def groups_by_bytes(bucket_bytes: Sequence[int], min_group_bytes: int) -> List[i
 
 
 def ddp_set_workgroups_per_cu(r: Reducer, n: int) -> None:
-    _check(lib().ddp_set_workgroups_per_cu(r.handle, int(n)))
+    _check(r._lib.ddp_set_workgroups_per_cu(r.handle, int(n)), r._lib)
 
 
 def ddp_get_launch_lds(r: Reducer) -> int:
     out = ctypes.c_int32()
-    _check(lib().ddp_get_launch_lds(r.handle, ctypes.byref(out)))
+    _check(r._lib.ddp_get_launch_lds(r.handle, ctypes.byref(out)), r._lib)
     return out.value
 
 
 def ddp_register_builtin_hook(r: Reducer, hook: int) -> None:
-    _check(lib().ddp_register_builtin_hook(r.handle, int(hook)))
+    _check(r._lib.ddp_register_builtin_hook(r.handle, int(hook)), r._lib)
 
 
 def ddp_get_bucket(r: Reducer, bucket: int):
     nbytes, off, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-    _check(lib().ddp_get_bucket(r.handle, bucket, ctypes.byref(nbytes), ctypes.byref(off), ctypes.byref(n)))
+    _check(r._lib.ddp_get_bucket(r.handle, bucket, ctypes.byref(nbytes), ctypes.byref(off), ctypes.byref(n)),
+           r._lib)
     return nbytes.value, off.value, n.value
 
 
 def ddp_get_bucket_params(r: Reducer, bucket: int) -> List[int]:
     n = ddp_get_bucket(r, bucket)[2]
     out = np.empty(max(n, 1), np.int32)
-    _check(lib().ddp_get_bucket_params(r.handle, bucket, out.ctypes.data))
+    _check(r._lib.ddp_get_bucket_params(r.handle, bucket, out.ctypes.data), r._lib)
     return [int(x) for x in out[:n]]
 
 
 def ddp_get_ready_order(r: Reducer) -> List[int]:
     out = np.empty(max(r.desc.numel.size, 1), np.int32)
     n = ctypes.c_int32()
-    _check(lib().ddp_get_ready_order(r.handle, out.ctypes.data, ctypes.byref(n)))
+    _check(r._lib.ddp_get_ready_order(r.handle, out.ctypes.data, ctypes.byref(n)), r._lib)
     return [int(x) for x in out[:n.value]]
 
 
 def ddp_get_launched(r: Reducer) -> int:
     n = ctypes.c_int32()
-    _check(lib().ddp_get_launched(r.handle, ctypes.byref(n)))
+    _check(r._lib.ddp_get_launched(r.handle, ctypes.byref(n)), r._lib)
     return n.value
 
 
 def ddp_set_timing(r: Reducer, enable: bool) -> None:
-    _check(lib().ddp_set_timing(r.handle, 1 if enable else 0))
+    _check(r._lib.ddp_set_timing(r.handle, 1 if enable else 0), r._lib)
 
 
 def ddp_get_timings(r: Reducer):
     """(first bucket, buckets covered, kernel ms) of every launch since timing
     was enabled, as three arrays."""
     n = ctypes.c_int32()
-    _check(lib().ddp_get_timings(r.handle, None, None, None, 0, ctypes.byref(n)))
+    _check(r._lib.ddp_get_timings(r.handle, None, None, None, 0, ctypes.byref(n)), r._lib)
     m = max(n.value, 1)
     b, c, ms = np.empty(m, np.int32), np.empty(m, np.int32), np.empty(m, np.float32)
-    _check(lib().ddp_get_timings(r.handle, b.ctypes.data, c.ctypes.data, ms.ctypes.data, n.value, ctypes.byref(n)))
+    _check(r._lib.ddp_get_timings(r.handle, b.ctypes.data, c.ctypes.data, ms.ctypes.data, n.value,
+                                  ctypes.byref(n)), r._lib)
     k = n.value
     return b[:k].copy(), c[:k].copy(), ms[:k].copy()
 

@@ -661,6 +661,34 @@ def test_reducer_dropped_without_destroy_is_released_by_its_finalizer():
     ddp.ddp_reducer_destroy(r2)
 
 
+def test_calls_on_a_reducer_go_to_the_library_that_created_it():
+    """Every binding call on a Reducer, and the error text it raises, goes
+    through the library instance that created it (a process may load more
+    than one build of the library)."""
+    r, plan, log = host_reducer([4, 4], 16, 16)
+
+    class Counting:
+        def __init__(self, L):
+            self.L, self.names = L, []
+
+        def __getattr__(self, name):
+            self.names.append(name)
+            return getattr(self.L, name)
+
+    r._lib = Counting(r._lib)
+    ddp.ddp_prepare_for_backward(r)
+    ddp.ddp_mark_ready(r, 1)
+    with pytest.raises(ddp.DDPError, match="only once"):
+        ddp.ddp_mark_ready(r, 1)
+    ddp.ddp_mark_ready_many(r, [0])
+    ddp.ddp_finish(r)
+    assert ddp.ddp_get_launched(r) == plan.n_buckets
+    ddp.ddp_reducer_destroy(r)
+    for name in ("ddp_prepare_for_backward", "ddp_mark_ready", "ddp_last_error", "ddp_mark_ready_many",
+                 "ddp_finish", "ddp_get_launched", "ddp_reducer_destroy"):
+        assert name in r._lib.names, name
+
+
 def test_error_texts_start_with_pytorchs_wording():
     """The three Reducer errors the pages quote keep PyTorch's wording at the
     start of the message [DDP-ch17 §17.6, §17.16], and list the gradients
