@@ -554,13 +554,6 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
     return DDP_OK;
 }
 
-// All-reduce of buckets [b0, b1) as issued by the reducer: the comm stream
-// first waits for everything queued on the compute stream (the buckets'
-// gradients were produced there), then the hook runs once per bucket, in
-// order, or the default reduction covers the whole range in one launch
-// [PTD-notes §2.3; MegatronDDP §3]. When the compute stream has already
-// drained, every gradient it produced is complete and visible, so the
-// cross-stream event (a few microseconds of queue latency) is skipped.
 // The replica masks of this backward go to the device once, on the comm
 // stream, ahead of its first reduction: the per-replica "used" tables reduced
 // over replicas (a bitwise OR) [DDP-ch17 §17.33; PTD-notes §3.2]. Masks equal
@@ -588,7 +581,14 @@ int upload_masks(ddp_reducer *r)
     return DDP_OK;
 }
 
-// Issues buckets [b0, b1); on failure *at is the first bucket not issued.
+// All-reduce of buckets [b0, b1) as issued by the reducer: the comm stream
+// first waits for everything queued on the compute stream (the buckets'
+// gradients were produced there), then the hook runs once per bucket, in
+// order, or the default reduction covers the whole range in one launch
+// [PTD-notes §2.3; MegatronDDP §3]. When the compute stream has already
+// drained, every gradient it produced is complete and visible, so the
+// cross-stream event (a few microseconds of queue latency) is skipped.
+// On failure *at is the first bucket not issued.
 int issue_buckets(ddp_reducer *r, int32_t b0, int32_t b1, int32_t *at)
 {
     *at = b0;
