@@ -233,6 +233,37 @@ class Session:
         self.last_issue_s = issue / max(steps, 1)
         return time.perf_counter() - t0
 
+    def record(self, **kw):
+        """The step recorded into a HIP graph from the compute stream
+        (stream capture) instead of run: the reducer's launches join the
+        recording through its stream-ordering events and its finish joins
+        the comm stream back. Only the wait-only backward can be recorded
+        (the GEMM backward is not)."""
+        torch = self.torch
+        if kw.get("backward_us", 0) > 0 and self.backward_kind != "spin":
+            raise ValueError("only the wait-only backward is recorded into a graph")
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.compute):
+            graph.capture_begin()
+            try:
+                self.step(**kw)
+            finally:
+                graph.capture_end()
+        return graph
+
+    def timed_replays(self, graph, steps: int):
+        """Wall time of `steps` replays of a recorded step, launched back to
+        back on the compute stream."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.compute):
+            for _ in range(steps):
+                graph.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
 
 def bucket_alg_of(session, wl):
     """Algorithmic bytes of each bucket's reduction: per element, 4 bytes (6
@@ -478,12 +509,23 @@ def run_sweep(args):
             t_pb = s.timed(k, per_bucket=True) / k
             s.timed(2)
             t_co = s.timed(k) / k
+            # the same one-launch-per-bucket step recorded into a HIP graph
+            graph = s.record(per_bucket=True)
+            s.timed_replays(graph, 2)
+            t_gr = s.timed_replays(graph, k) / k
+            del graph
             us = args.backward_ms * 1e3
             s.timed(1, backward_us=us, backward_only=True)
             t_bw = s.timed(args.overlap_steps, backward_us=us, backward_only=True) / args.overlap_steps
             s.timed(1, backward_us=us)
             t_ov = s.timed(args.overlap_steps, backward_us=us) / args.overlap_steps
             t_se = s.timed(args.overlap_steps, backward_us=us, serial=True) / args.overlap_steps
+            t_gov = None
+            if args.backward_kind == "spin":
+                graph = s.record(backward_us=us)
+                s.timed_replays(graph, 1)
+                t_gov = s.timed_replays(graph, args.overlap_steps) / args.overlap_steps
+                del graph
             row = {"world": W, "cap_mib": cap, "buckets": s.plan.n_buckets,
                    "bytes_per_step": nbytes,
                    "per_bucket_launch_ms": round(t_pb * 1e3, 4), "per_bucket_launch_GBps": round(nbytes / t_pb / 1e9, 1),
@@ -491,7 +533,12 @@ def run_sweep(args):
                    "backward_alone_ms": round(t_bw * 1e3, 3),
                    "overlapped_step_ms": round(t_ov * 1e3, 3),
                    "serial_step_ms": round(t_se * 1e3, 3),
-                   "exposed_ms": round((t_ov - t_bw) * 1e3, 3)}
+                   "exposed_ms": round((t_ov - t_bw) * 1e3, 3),
+                   "graph_per_bucket_launch_ms": round(t_gr * 1e3, 4),
+                   "graph_per_bucket_launch_GBps": round(nbytes / t_gr / 1e9, 1)}
+            if t_gov is not None:
+                row.update({"graph_overlapped_step_ms": round(t_gov * 1e3, 3),
+                            "graph_exposed_ms": round((t_gov - t_bw) * 1e3, 3)})
             if args.sweep_group_mib > 0 and s.plan.n_buckets > 1:
                 # bucket groups of at least sweep_group_mib: one launch per group
                 import bucketed_gradient_all_amd as ddp
@@ -693,6 +740,18 @@ def main():
                          "kernel_GBps_per_bucket": per_bucket if len(per_bucket) <= 16 else None,
                          "kernel_GBps_all": round(sum(bucket_alg) * args.steps / (float(pms.sum()) / 1e3) / 1e9, 1)
                          if pms.size else None}
+    # the same step recorded into a HIP graph (stream capture) and replayed:
+    # the launches, their waits on the compute stream and the finish, without
+    # the host's per-launch calls. Unused-parameter masks are host state a
+    # replay cannot change, so that configuration is not recorded.
+    per_bucket_graph = None
+    if used is None:
+        graph = s.record(per_bucket=True)
+        s.timed_replays(graph, 5)
+        g_elapsed = s.timed_replays(graph, args.steps) / args.steps
+        del graph
+        per_bucket_graph = {"ms_per_step": round(g_elapsed * 1e3, 4),
+                            "GBps": round(bytes_per_step / g_elapsed / 1e9, 2)}
 
     def overlap_of(kind):
         """The step with a synthetic backward of backward_ms on the compute
@@ -799,6 +858,7 @@ def main():
                      "achieved_mall_scrubbed": (round(scrubbed[0] / scrubbed[1] / 1e9, 1)
                                                 if scrubbed is not None else None)},
         "per_bucket_launch": per_bucket_launch,
+        "per_bucket_launch_graph": per_bucket_graph,
         "overlap": overlap,
         "overlap_gemm_backward": overlap_gemm,
         "plain_layout": plain,

@@ -64,6 +64,18 @@ int hip_fail(const char *what, hipError_t e) noexcept
     return DDP_ERR_HIP;
 }
 
+// *captured: whether work enqueued on s is being recorded into a HIP graph
+// (stream capture) rather than run. The null stream cannot be captured.
+hipError_t is_captured(hipStream_t s, bool *captured) noexcept
+{
+    *captured = false;
+    if (!s) return hipSuccess;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(s, &st);
+    *captured = e == hipSuccess && st != hipStreamCaptureStatusNone;
+    return e;
+}
+
 // Every entry point runs its body through this: the C ABI never lets an
 // exception out. Host memory exhaustion (std::bad_alloc from a container or
 // a message) becomes DDP_ERR_NOMEM; anything else DDP_ERR_INVALID.
@@ -503,6 +515,11 @@ int enqueue_reduce(ddp_reducer *r, int32_t b0, int32_t b1, hipStream_t s)
     const size_t rec = r->timed.size();
     const size_t slot = rec % kTimingSlots;
     if (r->timing) {
+        bool captured = false;
+        if ((e = is_captured(s, &captured)) != hipSuccess) return hip_fail("stream capture status", e);
+        if (captured)
+            return fail(DDP_ERR_INVALID, "per-launch timing reads its events on the host: it is not available "
+                                         "while the stream is captured into a graph");
         if (rec >= kTimingSlots) {
             const int rc = resolve_timings(r, rec - kTimingSlots + 1);
             if (rc != DDP_OK) return rc;
@@ -598,8 +615,26 @@ int issue_buckets(ddp_reducer *r, int32_t b0, int32_t b1, int32_t *at)
         ddp_reducer *r;
         ~Reset() { r->beside_backward = false; }
     } reset{r};
+    bool captured = false;
+    if (r->device) {
+        const hipError_t e = is_captured(r->compute, &captured);
+        if (e != hipSuccess) return hip_fail("stream capture status", e);
+        // Checked before anything is enqueued, so a refused launch leaves the
+        // capture as it was. Replays of a graph cannot change the replica
+        // masks, which are host state of each backward, nor read timing
+        // events on the host.
+        if (captured && r->pv.find_unused)
+            return fail(DDP_ERR_INVALID, "unused-parameter detection is not available while the compute stream "
+                                         "is captured into a graph (the replica masks are host state)");
+        if (captured && r->timing)
+            return fail(DDP_ERR_INVALID, "per-launch timing reads its events on the host: it is not available "
+                                         "while the compute stream is captured into a graph");
+    }
     if (r->device && r->compute != r->comm) {
-        hipError_t e = hipStreamQuery(r->compute);
+        // Under stream capture nothing has run and a stream query would break
+        // the capture: the launch always waits, and the graph keeps that wait
+        // as an edge from the compute stream's work to the reduction.
+        hipError_t e = captured ? hipErrorNotReady : hipStreamQuery(r->compute);
         if (e == hipErrorNotReady) {
             // The compute stream has work queued. A launch that does not hold
             // the backward's last bucket runs beside the backward kernels
@@ -1051,6 +1086,14 @@ int ddp_bucket_reduce_impl(ddp_reducer *r, int32_t bucket, void *stream)
 int ddp_finish_impl(ddp_reducer *r, int32_t host_blocking)
 {
     if (!r) return fail(DDP_ERR_INVALID, "reducer is NULL");
+    if (host_blocking && r->device) {
+        bool captured = false;
+        const hipError_t e = is_captured(r->compute, &captured);
+        if (e != hipSuccess) return hip_fail("stream capture status", e);
+        if (captured)
+            return fail(DDP_ERR_INVALID, "a host-blocking finish cannot wait while the compute stream is "
+                                         "captured into a graph; nothing was changed");
+    }
     if (!r->sync) {           // no_sync: nothing was reduced, the used tables keep accumulating
         r->finished = true;
         return DDP_OK;

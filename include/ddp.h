@@ -234,7 +234,18 @@ int ddp_prepare_for_backward(ddp_reducer *r);
  * DDP_ERR_HIP, DDP_ERR_HOOK (a launch failed; the mark itself counts). A
  * failed launch ends the backward's reductions: the buckets from the one
  * that failed on are not reduced, every later launch in the same backward is
- * refused with the same code, and ddp_finish reports the failure. */
+ * refused with the same code, and ddp_finish reports the failure.
+ * Stream capture: while the compute stream is being recorded into a HIP
+ * graph (hipStreamBeginCapture, or a framework's graph capture on that
+ * stream), a launch never queries the compute stream. It always waits on it
+ * through the reducer's event, which the graph keeps as an edge from the
+ * recorded backward to the reduction, and every launch but the one holding
+ * the last bucket takes the shape for running beside a backward. Per-launch
+ * timing and unused-parameter detection are refused there (DDP_ERR_INVALID,
+ * before anything is enqueued, so the capture stays usable): a replay cannot
+ * read timing events on the host nor change the replica masks. Create the
+ * reducer before the capture begins (creation uploads its tables
+ * synchronously). */
 int ddp_mark_ready(ddp_reducer *r, int32_t param);
 
 /* ddp_mark_ready for params[0], params[1], ... in that order, in one call
@@ -278,7 +289,10 @@ int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
  * host_blocking != 0 the host also waits for the reductions to complete.
  * If a launch of this backward failed, it returns that launch's error code
  * (DDP_ERR_HOOK or DDP_ERR_HIP), naming the buckets that were not reduced,
- * and ends the backward. */
+ * and ends the backward. While the compute stream is being recorded into a
+ * HIP graph, host_blocking != 0 is refused (DDP_ERR_INVALID) and nothing
+ * changes; a non-blocking finish records the comm stream's join into the
+ * compute stream, which the capture needs before it ends. */
 int ddp_finish(ddp_reducer *r, int32_t host_blocking);
 
 /* no_sync [L15 §4.1; PTD-notes §2.2.4]: with sync == 0, the backward passes

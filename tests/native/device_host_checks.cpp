@@ -7,6 +7,11 @@
 //  * unused-parameter detection with a reduction on another stream: that
 //    stream waits for the mask upload on the comm stream, and the comm
 //    stream (so the next upload) waits for the reduction;
+//  * stream capture (a HIP graph recorded from the compute stream): the
+//    compute stream is never queried, every launch waits on it by an event,
+//    finish joins the comm stream back, and what a replay could not honour
+//    (timing, unused detection, a host-blocking finish) is refused before
+//    anything is enqueued;
 //  * host memory exhaustion: with operator new failing after k allocations,
 //    every entry point returns DDP_OK or DDP_ERR_NOMEM, nothing leaks, no
 //    event is left behind, and a launch that could not be issued is
@@ -426,11 +431,89 @@ void check_launch_occupancy()
     fake::g_stream_query = hipErrorNotReady;
 }
 
+// Stream capture: the launch path must not query the compute stream (a
+// query of a capturing stream breaks the capture). Each launch waits on the
+// compute stream by an event, the launches of a backward but the last take
+// the shape for running beside one, and finish makes the compute stream wait
+// for the comm stream (the graph's join). Timing, unused detection and a
+// host-blocking finish are refused with nothing enqueued.
+void check_capture()
+{
+    fake::g_logging = true;
+    Model m(8, 12, 6000, false, 41);
+    ddp_reducer *r = nullptr;
+    expect(ddp_reducer_create(&m.d, &r) == DDP_OK, "capture: create");
+    int32_t tuned = 0;
+    expect(ddp_get_launch_lds(r, &tuned) == DDP_OK, "capture: launch LDS");
+    const unsigned one = 83968;   // one per CU
+    fake::g_stream_query = hipSuccess;   // a query would (wrongly) report a drained stream
+    fake::g_capturing = true;
+    fake::g_stream_queries = 0;
+    fake::reset_log();
+    expect(backward(r, m) == DDP_OK, "capture: backward");
+    expect(fake::g_stream_queries == 0, "capture: the compute stream was queried");
+    int launches = 0, waits = 0;
+    bool waited_before_each = true, shapes = true;
+    bool compute_waited = false;
+    for (size_t i = 0; i < fake::g_log.size(); ++i) {
+        const fake::Call &c = fake::g_log[i];
+        if (!std::strcmp(c.what, "wait") && c.stream == kComm) ++waits;
+        if (!std::strcmp(c.what, "launch")) {
+            waited_before_each &= waits == launches + 1 && c.stream == kComm;
+            const bool last = launches == m.B - 1;
+            shapes &= c.lds == (last ? unsigned(tuned) : one) && c.pair == !last;
+            ++launches;
+        }
+        if (!std::strcmp(c.what, "wait") && c.stream == kCompute) compute_waited = launches == m.B;
+    }
+    expect(launches == m.B, "capture: one launch per bucket");
+    expect(waited_before_each, "capture: every launch waits on the compute stream");
+    expect(shapes, "capture: beside-backward shape but for the last launch");
+    expect(compute_waited, "capture: finish joins the comm stream into the compute stream");
+
+    // a host-blocking finish is refused and changes nothing
+    expect(ddp_prepare_for_backward(r) == DDP_OK, "capture: prepare");
+    for (int p = m.P - 1; p >= 0; --p) expect(ddp_mark_ready(r, p) == DDP_OK, "capture: mark");
+    fake::reset_log();
+    expect(ddp_finish(r, 1) == DDP_ERR_INVALID, "capture: host-blocking finish refused");
+    expect(fake::g_log.empty(), "capture: the refused finish enqueued something");
+    expect(ddp_finish(r, 0) == DDP_OK, "capture: finish without blocking after the refusal");
+
+    // timing is refused at the first launch, before the wait
+    expect(ddp_set_timing(r, 1) == DDP_OK, "capture: timing on");
+    expect(ddp_prepare_for_backward(r) == DDP_OK, "capture: prepare (timing)");
+    fake::reset_log();
+    int rc = DDP_OK;
+    for (int p = m.P - 1; p >= 0 && rc == DDP_OK; --p) rc = ddp_mark_ready(r, p);
+    expect(rc == DDP_ERR_INVALID, "capture: timed launch refused");
+    expect(fake::g_log.empty(), "capture: the refused launch enqueued something");
+    expect(ddp_set_timing(r, 0) == DDP_OK, "capture: timing off");
+    expect(ddp_prepare_for_backward(r) == DDP_OK, "capture: prepare after the refusal");
+    expect(backward(r, m) == DDP_OK, "capture: backward after the refusal");
+    expect(ddp_reducer_destroy(r) == DDP_OK, "capture: destroy");
+
+    // unused-parameter detection is refused the same way
+    Model mu(4, 10, 4000, true, 43);
+    fake::g_capturing = false;
+    expect(ddp_reducer_create(&mu.d, &r) == DDP_OK, "capture: create (unused detection)");
+    fake::g_capturing = true;
+    expect(ddp_prepare_for_backward(r) == DDP_OK, "capture: prepare (unused detection)");
+    fake::reset_log();
+    rc = DDP_OK;
+    for (int p = mu.P - 1; p >= 0 && rc == DDP_OK; --p) rc = ddp_mark_ready(r, p);
+    expect(rc == DDP_ERR_INVALID, "capture: unused detection refused");
+    expect(fake::g_log.empty(), "capture: the refused launch (unused detection) enqueued something");
+    fake::g_capturing = false;
+    expect(ddp_reducer_destroy(r) == DDP_OK, "capture: destroy (unused detection)");
+    fake::g_stream_query = hipErrorNotReady;
+}
+
 }  // namespace
 
 int main()
 {
     check_launch_occupancy();
+    check_capture();
     check_timing_ring();
     check_foreign_stream_masks();
     check_out_of_memory();

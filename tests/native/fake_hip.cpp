@@ -28,6 +28,8 @@ long g_stamp = 0;
 hipError_t g_stream_query = hipErrorNotReady;
 hipError_t g_event_query = hipSuccess;
 bool g_logging = true;
+bool g_capturing = false;
+long g_stream_queries = 0;
 
 namespace {
 
@@ -115,7 +117,15 @@ hipError_t hipStreamWaitEvent(hipStream_t stream, hipEvent_t event, unsigned int
 
 hipError_t hipStreamQuery(hipStream_t)
 {
+    ++fake::g_stream_queries;
     return fake::g_stream_query;
+}
+
+hipError_t hipStreamIsCapturing(hipStream_t stream, hipStreamCaptureStatus *status)
+{
+    if (!status) return hipErrorInvalidValue;
+    *status = stream && fake::g_capturing ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
+    return hipSuccess;
 }
 
 hipError_t hipEventQuery(hipEvent_t event)

@@ -23,6 +23,8 @@ extern long g_max_live_events;   // the most ever alive at once
 extern hipError_t g_stream_query;   // what hipStreamQuery returns (default: hipErrorNotReady)
 extern hipError_t g_event_query;    // what hipEventQuery returns for a recorded event (default: hipSuccess)
 extern bool g_logging;              // append calls to g_log
+extern bool g_capturing;            // what hipStreamIsCapturing reports for every non-null stream
+extern long g_stream_queries;       // hipStreamQuery calls so far
 
 long stamp_of(hipEvent_t e);
 void reset_log();

@@ -1,6 +1,7 @@
-"""GPU: bench.py end to end on the tiny workload (a few steps of every pass)
-and the stream probe on small buffers, as separate processes: the JSON line
-carries the fields its reader relies on."""
+"""GPU: bench.py end to end on the tiny workload (a few steps of every pass),
+a two-cap bucket-size sweep at W = 2 and the stream probe on small buffers,
+as separate processes: the JSON lines carry the fields their reader relies
+on."""
 import json
 import os
 import subprocess
@@ -28,9 +29,10 @@ def test_bench_line_on_the_tiny_workload(extra):
     assert len(lines) == 1
     d = lines[0]
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "dtype",
-              "config", "roofline", "cpu_baseline", "per_bucket_launch", "overlap", "overlap_gemm_backward",
-              "plain_layout"):
+              "config", "roofline", "cpu_baseline", "per_bucket_launch", "per_bucket_launch_graph", "overlap",
+              "overlap_gemm_backward", "plain_layout"):
         assert k in d, k
+    assert d["per_bucket_launch_graph"]["GBps"] > 0
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0
     assert d["config"]["workload"].startswith("tiny") and d["config"]["replica_layout"].startswith("slots of")
     r = d["roofline"]
@@ -45,3 +47,16 @@ def test_stream_probe_lines():
     for d in lines:
         for kind in ("read_GBps", "write_GBps", "copy_GBps", "accum_GBps"):
             assert set(d[kind]) == {"1", "2", "0"} and all(v > 0 for v in d[kind].values())
+
+
+def test_sweep_rows_with_graph_replays():
+    lines = _run(["--sweep", "--sweep-worlds", "2", "--sweep-caps", "0,25", "--overlap-steps", "1",
+                  "--backward-ms", "2", "--sweep-group-mib", "25"], timeout=400)
+    assert len(lines) == 1
+    rows = lines[0]["rows"]
+    assert [(r["world"], r["cap_mib"]) for r in rows] == [(2, 0), (2, 25)]
+    assert rows[0]["buckets"] == 6000
+    for r in rows:
+        for k in ("per_bucket_launch_GBps", "coalesced_GBps", "graph_per_bucket_launch_GBps", "overlapped_step_ms",
+                  "graph_overlapped_step_ms"):
+            assert r[k] > 0, k
