@@ -1070,6 +1070,13 @@ int ddp_bucket_reduce_impl(ddp_reducer *r, int32_t bucket, void *stream)
     // next rewrite after it.
     const bool foreign = r->device && r->pv.find_unused && s != r->comm;
     hipError_t e = hipSuccess;
+    if (r->device && r->pv.find_unused) {
+        bool captured = false;
+        if ((e = is_captured(s, &captured)) != hipSuccess) return hip_fail("stream capture status", e);
+        if (captured)
+            return fail(DDP_ERR_INVALID, "unused-parameter detection is not available while the stream is "
+                                         "captured into a graph (the replica masks are host state)");
+    }
     if (foreign) {
         e = hipEventRecord(r->ev_tables, r->comm);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, r->ev_tables, 0);

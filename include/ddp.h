@@ -280,7 +280,9 @@ int ddp_mark_ready_many(ddp_reducer *r, const int32_t *params, int32_t n, int32_
  * masks travel in the segment table, which the comm stream rewrites, so on
  * any other stream the reduction is made to wait for the work queued so far
  * on the comm stream, and the comm stream to wait for the reduction (two
- * events; results do not depend on the stream). */
+ * events; results do not depend on the stream). On a stream being recorded
+ * into a HIP graph, a reducer with unused-parameter detection, or with
+ * per-launch timing on, refuses (DDP_ERR_INVALID, nothing enqueued). */
 int ddp_bucket_reduce(ddp_reducer *r, int32_t bucket, void *stream);
 
 /* End of backward [DDP-ch17 §17.41; MegatronDDP §5]: checks that every bucket

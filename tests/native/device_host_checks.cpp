@@ -503,6 +503,8 @@ void check_capture()
     for (int p = mu.P - 1; p >= 0 && rc == DDP_OK; --p) rc = ddp_mark_ready(r, p);
     expect(rc == DDP_ERR_INVALID, "capture: unused detection refused");
     expect(fake::g_log.empty(), "capture: the refused launch (unused detection) enqueued something");
+    expect(ddp_bucket_reduce(r, 0, kOther) == DDP_ERR_INVALID && fake::g_log.empty(),
+           "capture: a standalone reduction with unused detection refused, nothing enqueued");
     fake::g_capturing = false;
     expect(ddp_reducer_destroy(r) == DDP_OK, "capture: destroy (unused detection)");
     fake::g_stream_query = hipErrorNotReady;

@@ -214,8 +214,11 @@ def test_refusals_leave_the_capture_usable():
             ddp.ddp_prepare_for_backward(run.r)
             with pytest.raises(ddp.DDPError) as e:
                 ddp.ddp_mark_ready_many(run.r, list(range(len(run.wl.numel) - 1, -1, -1)))
+            with pytest.raises(ddp.DDPError) as e2:   # a standalone reduction on the captured stream
+                ddp.ddp_bucket_reduce(run.r, 0, run.compute.cuda_stream)
         finally:
             g.capture_end()
     assert e.value.code == ddp.DDP_ERR_INVALID and "unused" in e.value.msg
+    assert e2.value.code == ddp.DDP_ERR_INVALID and "unused" in e2.value.msg
     del g
     run.close()
