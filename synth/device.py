@@ -14,7 +14,6 @@ from __future__ import annotations
 
 from typing import List, Optional, Sequence
 
-import numpy as np
 
 from . import fill_dev, key, scale_for
 from .workloads import (IN_BF16_ACCUM_F32, IN_F32_COPY, IN_F32_VIEW, STREAM_GRAD, STREAM_MAIN, STREAM_WGRAD,

@@ -6,7 +6,6 @@ import random
 import re
 import sys
 
-import numpy as np
 import pytest
 
 import bucketed_gradient_all_amd as ddp

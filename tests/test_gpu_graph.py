@@ -10,7 +10,6 @@ the NaNs. Each replay is compared bit for bit with an eager step on the same
 inputs and with the oracle, with eager work and synchronisation between
 replays. What a replay cannot honour (per-launch timing, unused-parameter
 masks, a host-blocking finish) is refused without breaking the capture."""
-import numpy as np
 import pytest
 
 from test_gpu_parity import Run, _torch, assert_bits, owned_mask, say

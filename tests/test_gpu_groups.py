@@ -1,6 +1,5 @@
 """GPU: bucket groups [MegatronDDP §3] issue one launch per complete group,
 in order, with results bit-exact against the oracle."""
-import numpy as np
 import pytest
 
 from test_gpu_parity import Run, _torch, check_full, say

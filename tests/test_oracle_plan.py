@@ -1,6 +1,5 @@
 """Pins of the oracle's bucket plan (O1) against the pages' printed layouts,
 special cases and an independent prefix-sum formulation."""
-import itertools
 import random
 import sys
 
