@@ -32,9 +32,10 @@ class Graphed:
     """A Run whose backward (gradient copies + ready marks + finish) is
     recorded into a graph."""
 
-    def __init__(self, wl, per_bucket, collective=0, static=False):
+    def __init__(self, wl, per_bucket, collective=0, static=False, hook=0, groups=False):
         self.run = run = Run(wl, collective=collective)
         self.torch, self.ddp, self.wl = run.torch, run.ddp, wl
+        self.hook = hook
         if static:
             ddp = run.ddp
             ddp.ddp_reducer_destroy(run.r)
@@ -43,6 +44,9 @@ class Graphed:
                             compute_stream=run.compute.cuda_stream, comm_stream=run.comm.cuda_stream,
                             collective=collective)
             run.r = ddp.ddp_reducer_create_static(desc)
+        run.ddp.ddp_register_builtin_hook(run.r, hook)
+        if groups:   # bucket groups of two: one launch per group
+            run.ddp.ddp_set_bucket_groups(run.r, list(range(0, run.plan.n_buckets, 2)))
         inp = run.inputs
         self.per_bucket = per_bucket
         self.src = [g.clone() for g in inp.grads]
@@ -127,7 +131,7 @@ class Graphed:
 def _check_against_oracle(gr, seed, got, before, collective):
     from expect import expected_flat, host_threads, oracle_plan
     wl = gr.wl
-    want = expected_flat(wl, oracle_plan(wl), seed, nthreads=host_threads())
+    want = expected_flat(wl, oracle_plan(wl), seed, nthreads=host_threads(), hook=gr.hook)
     for w in range(wl.world):
         if collective:
             m = owned_mask(gr.run, w)
@@ -137,19 +141,21 @@ def _check_against_oracle(gr, seed, got, before, collective):
             assert_bits(got[w], want, f"{wl.name} seed {seed} replica {w} (replay against the oracle)")
 
 
-@pytest.mark.parametrize("W,mode,per_bucket,collective,static", [
-    (8, 0, True, 0, False),     # one launch per bucket: the two-tile shape beside the backward
-    (8, 0, False, 0, False),    # one coalesced launch
-    (16, 2, True, 0, False),    # bf16 wgrads accumulated into fp32 main_grad
-    (5, 0, True, 1, False),     # reduce-scatter
-    (12, 0, True, 0, False),    # a partial 16-slot instance
-    (4, 2, True, 0, True),      # the static-table (no-allocation) reducer
+@pytest.mark.parametrize("W,mode,per_bucket,collective,static,hook,groups", [
+    (8, 0, True, 0, False, 0, False),     # one launch per bucket: the two-tile shape beside the backward
+    (8, 0, False, 0, False, 0, False),    # one coalesced launch
+    (16, 2, True, 0, False, 0, False),    # bf16 wgrads accumulated into fp32 main_grad
+    (5, 0, True, 1, False, 0, False),     # reduce-scatter
+    (12, 0, True, 0, False, 0, False),    # a partial 16-slot instance
+    (4, 2, True, 0, True, 0, False),      # the static-table (no-allocation) reducer
+    (8, 0, True, 0, False, 1, False),     # the bf16 compression hook
+    (6, 2, True, 1, False, 2, True),      # fp16 hook, reduce-scatter, bf16 mode, bucket groups of two
 ])
-def test_recorded_backward_replays_match_eager_and_oracle(W, mode, per_bucket, collective, static):
-    wl = _workload(f"graph_w{W}_m{mode}", SHAPES, W, mode, 120000, 900 + W + 10 * mode)
-    say(f"case graph {wl.name} per_bucket={per_bucket} collective={collective} static={static} "
-        f"P={len(wl.numel)} elements={wl.total_numel}")
-    gr = Graphed(wl, per_bucket, collective=collective, static=static)
+def test_recorded_backward_replays_match_eager_and_oracle(W, mode, per_bucket, collective, static, hook, groups):
+    wl = _workload(f"graph_w{W}_m{mode}", SHAPES, W, mode, 120000, 900 + W + 10 * mode + 100 * hook)
+    say(f"case graph {wl.name} per_bucket={per_bucket} collective={collective} static={static} hook={hook} "
+        f"groups={groups} P={len(wl.numel)} elements={wl.total_numel}")
+    gr = Graphed(wl, per_bucket, collective=collective, static=static, hook=hook, groups=groups)
     assert gr.run.plan.n_buckets >= 3
     gr.set_inputs(1)
     gr.record()
