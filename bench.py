@@ -740,18 +740,19 @@ def main():
                          "kernel_GBps_per_bucket": per_bucket if len(per_bucket) <= 16 else None,
                          "kernel_GBps_all": round(sum(bucket_alg) * args.steps / (float(pms.sum()) / 1e3) / 1e9, 1)
                          if pms.size else None}
-    # the same step recorded into a HIP graph (stream capture) and replayed:
-    # the launches, their waits on the compute stream and the finish, without
-    # the host's per-launch calls. Unused-parameter masks are host state a
-    # replay cannot change, so that configuration is not recorded.
-    per_bucket_graph = None
-    if used is None:
-        graph = s.record(per_bucket=True)
+    # the step and the one-launch-per-bucket step recorded into a HIP graph
+    # (stream capture) and replayed back to back: the launches, their waits on
+    # the compute stream and the finish, without the host's calls.
+    # Unused-parameter masks are host state a replay cannot change, so that
+    # configuration is not recorded.
+    def replayed(**kw):
+        graph = s.record(**kw)
         s.timed_replays(graph, 5)
-        g_elapsed = s.timed_replays(graph, args.steps) / args.steps
+        t = s.timed_replays(graph, args.steps) / args.steps
         del graph
-        per_bucket_graph = {"ms_per_step": round(g_elapsed * 1e3, 4),
-                            "GBps": round(bytes_per_step / g_elapsed / 1e9, 2)}
+        return {"ms_per_step": round(t * 1e3, 4), "GBps": round(bytes_per_step / t / 1e9, 2)}
+
+    graph_replay = None if used is not None else {"step": replayed(), "per_bucket_launch": replayed(per_bucket=True)}
 
     def overlap_of(kind):
         """The step with a synthetic backward of backward_ms on the compute
@@ -858,7 +859,7 @@ def main():
                      "achieved_mall_scrubbed": (round(scrubbed[0] / scrubbed[1] / 1e9, 1)
                                                 if scrubbed is not None else None)},
         "per_bucket_launch": per_bucket_launch,
-        "per_bucket_launch_graph": per_bucket_graph,
+        "graph_replay": graph_replay,
         "overlap": overlap,
         "overlap_gemm_backward": overlap_gemm,
         "plain_layout": plain,

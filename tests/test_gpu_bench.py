@@ -29,10 +29,10 @@ def test_bench_line_on_the_tiny_workload(extra):
     assert len(lines) == 1
     d = lines[0]
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "dtype",
-              "config", "roofline", "cpu_baseline", "per_bucket_launch", "per_bucket_launch_graph", "overlap",
+              "config", "roofline", "cpu_baseline", "per_bucket_launch", "graph_replay", "overlap",
               "overlap_gemm_backward", "plain_layout"):
         assert k in d, k
-    assert d["per_bucket_launch_graph"]["GBps"] > 0
+    assert d["graph_replay"]["step"]["GBps"] > 0 and d["graph_replay"]["per_bucket_launch"]["GBps"] > 0
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0
     assert d["config"]["workload"].startswith("tiny") and d["config"]["replica_layout"].startswith("slots of")
     r = d["roofline"]
